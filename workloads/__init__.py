@@ -1,0 +1,377 @@
+"""Seeded synthetic inputs shaped like the pages' serving workloads.
+
+This module draws numbers and lays out buffers; it holds none of the method's
+arithmetic (no slot formula, no attention).  Both the HIP path and the CPU
+oracle consume what it returns, and each side executes the returned *plan*
+with its own code:
+
+    setup: a list of ops run once (history writes, and copy-on-write for the
+           observable-CoW variant of the shared-prefix workload)
+    step:  the ops of one decode step, timed by the benchmark
+           ([copy,] write of the new token per sequence, decode attention)
+
+An op is ``("write", Write)`` -- compute the slot of every (sequence, position)
+pair through the named block table, then store K/V there -- or
+``("copy", pairs)``.  Pools start as all-NaN bit patterns, so every slot and
+block the plan never writes stays poisoned; table padding is -1.
+
+Random draws: ``numpy.random.default_rng(SeedSequence([188, config_id]))``,
+drawn in the fixed order context lengths -> block permutation -> Q -> history
+K -> history V -> new-token K -> new-token V.  float32 draws are rounded to
+bfloat16 by round-to-nearest-even once, here, so both sides see the same bits.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+BF16_NAN = np.uint16(0x7FC0)
+F32_NAN_BITS = np.uint32(0x7FC00000)
+SEED_ROOT = 188
+
+
+# ---------------------------------------------------------------------------
+# element encodings
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def draw_normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """N(0,1) float32 draws in the element encoding of ``dtype``."""
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if dtype == BF16:
+        return f32_to_bf16_bits(x)
+    return x
+
+
+def nan_pool(shape, dtype: str) -> np.ndarray:
+    if dtype == BF16:
+        return np.full(shape, BF16_NAN, dtype=np.uint16)
+    return np.full(shape, F32_NAN_BITS, dtype=np.uint32).view(np.float32)
+
+
+def elem_bytes(dtype: str) -> int:
+    return 2 if dtype == BF16 else 4
+
+
+# ---------------------------------------------------------------------------
+# plan containers
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Write:
+    """Tokens to store: token j is logical position ``positions[j]`` of
+    sequence ``seq_ids[j]``, addressed through block table ``table``."""
+    table: str
+    seq_ids: np.ndarray        # int32 [T]
+    positions: np.ndarray      # int32 [T]
+    k: np.ndarray              # [T][Hkv][D] element bits
+    v: np.ndarray
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    scale: float                       # a float32 value
+    q: np.ndarray                      # [S][Hq][D]
+    tables: dict                       # name -> int32 [S][MB]; "final" is decoded
+    context_lens: np.ndarray           # int32 [S], after the step's write
+    setup: list = field(default_factory=list)
+    step: list = field(default_factory=list)
+    partition_size: int = 0            # 0: the library picks
+    seed: tuple = ()
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    def empty_pools(self):
+        shape = (self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim)
+        return nan_pool(shape, self.dtype), nan_pool(shape, self.dtype)
+
+    # --- accounting (algorithmic bytes of one decode step) -----------------
+    def kv_bytes_read(self) -> int:
+        """K and V bytes the decode must read: every context token, once per KV
+        head (nothing is pruned or compressed)."""
+        return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads \
+            * self.head_dim * 2 * elem_bytes(self.dtype)
+
+    def decode_bytes(self) -> int:
+        """KV + query + fp32 output + block-table entries + context lengths."""
+        e = elem_bytes(self.dtype)
+        blocks = int(sum(math.ceil(int(c) / self.block_size) for c in self.context_lens))
+        return (self.kv_bytes_read()
+                + self.num_seqs * self.num_q_heads * self.head_dim * (e + 4)
+                + 4 * blocks + 4 * self.num_seqs)
+
+    def unique_kv_bytes(self) -> int:
+        """KV bytes of distinct physical blocks referenced by the final tables."""
+        bt = self.tables["final"]
+        ids = set()
+        for i in range(self.num_seqs):
+            nb = math.ceil(int(self.context_lens[i]) / self.block_size)
+            ids.update(int(x) for x in bt[i, :nb])
+        return len(ids) * self.num_kv_heads * self.block_size * self.head_dim \
+            * 2 * elem_bytes(self.dtype)
+
+
+def _rng(config_id) -> tuple:
+    seq = np.random.SeedSequence([SEED_ROOT, int(config_id)])
+    return np.random.default_rng(seq), (SEED_ROOT, int(config_id))
+
+
+def _blocks_for(ctx: int, block_size: int) -> int:
+    """Blocks a sequence of ``ctx`` tokens occupies (allocation bookkeeping)."""
+    return -(-ctx // block_size)
+
+
+def _positions(lengths, starts=None):
+    """Concatenated (seq_id, position) lists: sequence i gets positions
+    ``starts[i] .. starts[i]+lengths[i]-1``."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    if lengths.size == 0:
+        return np.zeros(0, np.int32), np.zeros(0, np.int32)
+    if starts is None:
+        starts = np.zeros_like(lengths)
+    seq_ids = np.repeat(np.arange(lengths.size, dtype=np.int32), lengths)
+    first = np.repeat(np.asarray(starts, dtype=np.int64) - np.concatenate(
+        [[0], np.cumsum(lengths)[:-1]]), lengths)
+    pos = (np.arange(int(lengths.sum()), dtype=np.int64) + first).astype(np.int32)
+    return seq_ids, pos
+
+
+def _history_kv(rng, n_tokens, num_kv_heads, head_dim, dtype, chunk_tokens=1 << 17):
+    """Draw history K then V in token chunks (bounded float32 temporaries)."""
+    out = []
+    for _ in range(2):
+        buf = np.empty((n_tokens, num_kv_heads, head_dim),
+                       dtype=np.uint16 if dtype == BF16 else np.float32)
+        for s in range(0, n_tokens, chunk_tokens):
+            e = min(n_tokens, s + chunk_tokens)
+            buf[s:e] = draw_normal(rng, (e - s, num_kv_heads, head_dim), dtype)
+        out.append(buf)
+    return out[0], out[1]
+
+
+# ---------------------------------------------------------------------------
+# generic decode workload (configs 1, 2, 3, 5 and custom test shapes)
+# ---------------------------------------------------------------------------
+
+def decode_workload(name, dtype, ctx_lens, num_q_heads, num_kv_heads, head_dim,
+                    block_size, *, rng, seed=(), pool_slack=1.1, num_blocks=None,
+                    max_blocks_per_seq=None, partition_size=0, scale=None,
+                    table_prefix_only=False):
+    """One new token per sequence at position ``ctx-1``; history ``0..ctx-2``
+    is written in setup.  Physical blocks come from a seeded permutation of the
+    pool, taken in (sequence, logical block) order.  ``ctx == 0`` sequences get
+    no token and no block."""
+    ctx = np.asarray(ctx_lens, dtype=np.int32)
+    S = ctx.size
+    need_each = np.array([_blocks_for(int(c), block_size) for c in ctx], dtype=np.int64)
+    need = int(need_each.sum())
+    if num_blocks is None:
+        num_blocks = max(1, math.ceil(pool_slack * need))
+    if num_blocks < need:
+        raise ValueError("pool smaller than the blocks needed")
+    mb = max_blocks_per_seq or (max(1, int(need_each.max())) if S else 1)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.full((S, mb), -1, dtype=np.int32)
+    cursor = 0
+    for i in range(S):
+        n = int(need_each[i])
+        bt[i, :n] = perm[cursor:cursor + n]
+        cursor += n
+    q = draw_normal(rng, (S, num_q_heads, head_dim), dtype)
+    hist_len = np.maximum(ctx.astype(np.int64) - 1, 0)
+    hk, hv = _history_kv(rng, int(hist_len.sum()), num_kv_heads, head_dim, dtype)
+    hs, hp = _positions(hist_len)
+    has_new = ctx > 0
+    new_seq = np.nonzero(has_new)[0].astype(np.int32)
+    new_pos = (ctx[has_new] - 1).astype(np.int32)
+    nk = draw_normal(rng, (new_seq.size, num_kv_heads, head_dim), dtype)
+    nv = draw_normal(rng, (new_seq.size, num_kv_heads, head_dim), dtype)
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(head_dim)))
+    wl = Workload(name=name, dtype=dtype, num_seqs=S, num_q_heads=num_q_heads,
+                  num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                  num_blocks=num_blocks, max_blocks_per_seq=mb, scale=scale, q=q,
+                  tables={"final": bt}, context_lens=ctx,
+                  partition_size=partition_size, seed=seed)
+    wl.setup.append(("write", Write("final", hs, hp, hk, hv)))
+    wl.step.append(("write", Write("final", new_seq, new_pos, nk, nv)))
+    wl.step.append(("decode", "final"))
+    return wl
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix / parallel-sampling workload (config 4)
+# ---------------------------------------------------------------------------
+
+def shared_prefix_workload(name, *, rng, seed=(), groups=32, samples=8, prefix=2048,
+                           tail_lo=64, tail_hi=512, num_q_heads=32, num_kv_heads=8,
+                           head_dim=128, block_size=16, dtype=BF16, pool_slack=1.1,
+                           cow_in_step=True):
+    """``groups`` prompts x ``samples`` samples.  Each group's prefix is written
+    once, through sample 0's table, into blocks every sample's table shares.
+    Copy-on-write gives every sample a private copy of the group's last prefix
+    block (logical block ``(prefix-1)//bs``), remapped in the "final" table.
+    Tails ``U[tail_lo, tail_hi]`` tokens are private.  ``ctx = prefix + tail``.
+
+    With ``cow_in_step`` the copy is part of every timed step (it is then
+    idempotent, which needs the prefix to end on a block boundary so that no
+    tail token lands in the copied block).  Otherwise the copy runs once in
+    setup, before the tails are written; with a prefix that ends inside a block
+    the first tail tokens then land in the private copy and the copy-on-write
+    is observable."""
+    S = groups * samples
+    tails = rng.integers(tail_lo, tail_hi, size=S, endpoint=True).astype(np.int64)
+    ctx = (prefix + tails).astype(np.int32)
+    n_prefix_blocks = _blocks_for(prefix, block_size)
+    last_shared = n_prefix_blocks - 1
+    if cow_in_step and prefix % block_size:
+        raise ValueError("a copy in every step needs a prefix on a block boundary")
+    total_blocks = np.array([_blocks_for(int(c), block_size) for c in ctx])
+    tail_blocks = total_blocks - n_prefix_blocks
+    unique_need = groups * n_prefix_blocks + S + int(tail_blocks.sum())
+    num_blocks = math.ceil(pool_slack * unique_need)
+    mb = int(total_blocks.max())
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    cursor = 0
+
+    def take(n):
+        nonlocal cursor
+        out = perm[cursor:cursor + n]
+        cursor += n
+        return out
+
+    pre = np.full((S, mb), -1, dtype=np.int32)
+    fin = np.full((S, mb), -1, dtype=np.int32)
+    pairs = np.empty((S, 2), dtype=np.int32)
+    for a in range(groups):
+        shared = take(n_prefix_blocks)
+        for s in range(samples):
+            i = a * samples + s
+            pre[i, :n_prefix_blocks] = shared
+            fin[i, :n_prefix_blocks] = shared
+            private = take(1)[0]
+            pairs[i] = (shared[last_shared], private)
+            fin[i, last_shared] = private
+            nt = int(tail_blocks[i])
+            fin[i, n_prefix_blocks:n_prefix_blocks + nt] = take(nt)
+            pre[i, n_prefix_blocks:n_prefix_blocks + nt] = fin[i, n_prefix_blocks:n_prefix_blocks + nt]
+    q = draw_normal(rng, (S, num_q_heads, head_dim), dtype)
+    pk, pv = _history_kv(rng, groups * prefix, num_kv_heads, head_dim, dtype)
+    tail_hist = tails - 1                       # the last token is the step's
+    tk, tv = _history_kv(rng, int(tail_hist.sum()), num_kv_heads, head_dim, dtype)
+    nk = draw_normal(rng, (S, num_kv_heads, head_dim), dtype)
+    nv = draw_normal(rng, (S, num_kv_heads, head_dim), dtype)
+    ps, pp = _positions(np.full(groups, prefix))
+    ps = (ps * samples).astype(np.int32)          # sample 0 of each group
+    ts, tp = _positions(tail_hist, starts=np.full(S, prefix))
+    scale = float(np.float32(1.0 / math.sqrt(head_dim)))
+    wl = Workload(name=name, dtype=dtype, num_seqs=S, num_q_heads=num_q_heads,
+                  num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                  num_blocks=num_blocks, max_blocks_per_seq=mb, scale=scale, q=q,
+                  tables={"pre": pre, "final": fin}, context_lens=ctx, seed=seed)
+    wl.setup.append(("write", Write("pre", ps, pp, pk, pv)))
+    if not cow_in_step:
+        wl.setup.append(("copy", pairs))
+    wl.setup.append(("write", Write("final", ts, tp, tk, tv)))
+    if cow_in_step:
+        wl.step.append(("copy", pairs))
+    wl.step.append(("write", Write("final", np.arange(S, dtype=np.int32),
+                                   (ctx - 1).astype(np.int32), nk, nv)))
+    wl.step.append(("decode", "final"))
+    wl.notes.update(groups=groups, samples=samples, prefix=prefix,
+                    prefix_blocks_shared=groups * n_prefix_blocks,
+                    cow_pairs=S)
+    return wl
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+CONFIG_NAMES = {
+    1: "tiny-fp32: S=4 ctx{5,16,17,40} Hq=Hkv=4 D=64 bs=16 NB=32",
+    2: "llama3-8b-decode: S=64 Hq=32 Hkv=8 D=128 bs=16 ctx~U[128,4096] bf16",
+    3: "llama3.1-70b-decode: S=256 Hq=64 Hkv=8 D=128 bs=16 ctx~lognormal(1024,0.8)[16,8192] bf16",
+    4: "shared-prefix: 32x8 samples prefix=2048 tails~U[64,512] Hq=32 Hkv=8 D=128 bs=16 bf16 +CoW",
+    5: "long-context: S=4 ctx=131072 Hq=64 Hkv=8 D=128 bs=32 NB=16384 part=512 bf16",
+}
+
+
+def make(config_id: int, *, small: bool = False) -> Workload:
+    """The workload of one of the five configurations.
+
+    ``small=True`` keeps every per-token shape (heads, head_dim, block_size,
+    dtype) and the length distribution's form but shrinks the batch and the
+    lengths so the oracle finishes in seconds; it still spans many 16-token
+    tiles, several split-K partitions and ragged tails."""
+    rng, seed = _rng(config_id if not small else 100 + config_id)
+    if config_id == 1:
+        ctx = np.array([5, 16, 17, 40], dtype=np.int32)
+        return decode_workload(CONFIG_NAMES[1], F32, ctx, 4, 4, 64, 16, rng=rng,
+                               seed=seed, num_blocks=32, max_blocks_per_seq=3)
+    if config_id == 2:
+        S, lo, hi = (64, 128, 4096) if not small else (6, 1, 700)
+        ctx = rng.integers(lo, hi, size=S, endpoint=True).astype(np.int32)
+        return decode_workload(CONFIG_NAMES[2] + (" [small]" if small else ""), BF16, ctx,
+                               32, 8, 128, 16, rng=rng, seed=seed,
+                               max_blocks_per_seq=_blocks_for(hi, 16))
+    if config_id == 3:
+        S, med, lo, hi = (256, 1024, 16, 8192) if not small else (12, 96, 1, 900)
+        raw = rng.lognormal(mean=math.log(med), sigma=0.8, size=S)
+        ctx = np.clip(np.rint(raw), lo, hi).astype(np.int32)
+        return decode_workload(CONFIG_NAMES[3] + (" [small]" if small else ""), BF16, ctx,
+                               64, 8, 128, 16, rng=rng, seed=seed,
+                               max_blocks_per_seq=_blocks_for(hi, 16))
+    if config_id == 4:
+        if not small:
+            return shared_prefix_workload(CONFIG_NAMES[4], rng=rng, seed=seed)
+        return shared_prefix_workload(CONFIG_NAMES[4] + " [small]", rng=rng, seed=seed,
+                                      groups=2, samples=4, prefix=96, tail_lo=5,
+                                      tail_hi=60)
+    if config_id == 5:
+        S, n, nb = (4, 131072, 16384) if not small else (2, 2080, 130)
+        ctx = np.full(S, n, dtype=np.int32)
+        return decode_workload(CONFIG_NAMES[5] + (" [small]" if small else ""), BF16, ctx,
+                               64, 8, 128, 32, rng=rng, seed=seed, num_blocks=nb,
+                               partition_size=512)
+    raise ValueError(f"no configuration {config_id}")
+
+
+def make_cow_observable(small: bool = True) -> Workload:
+    """Shared-prefix variant whose prefix ends inside a block, with the copy in
+    setup, so the first tail tokens of every sample land in its private copy."""
+    rng, seed = _rng(404 if small else 44)
+    if small:
+        return shared_prefix_workload("shared-prefix CoW-observable [small]", rng=rng,
+                                      seed=seed, groups=2, samples=4, prefix=88,
+                                      tail_lo=3, tail_hi=40, cow_in_step=False)
+    return shared_prefix_workload("shared-prefix CoW-observable prefix=2040", rng=rng,
+                                  seed=seed, prefix=2040, cow_in_step=False)
