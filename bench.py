@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the slot of every
+sequence's new token (pa_compute_slots), the KV write (pa_write_kv), the
+copy-on-write block copies when the workload has them (pa_copy_blocks), and
+paged decode attention (pa_decode_attention).  Inputs are resident in HBM
+before timing starts.  Each step reads a different one of several identical
+pool copies (together far larger than the 256 MB last-level cache), so no
+step is served from a cache warmed by the previous one.
+
+    python bench.py [--steps K] [--warmup W] [--config 2]
+
+prints ONE JSON line: KV GB/s of the whole step (`value`), seq-steps/s,
+the decode kernel's roofline fraction (HIP events around every decode
+launch on the stream it runs on) and the CPU oracle's rate on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seq-steps/sec"
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, AMD published peak
+LLC_BYTES = 256 << 20        # MI355X Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="workload (default 2: Llama-3-8B-shaped decode)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound on the oracle's timed CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle, as it stands, on the first sequences of the same workload
+    until `budget_s` seconds have passed (at least one sequence)."""
+    import resource
+
+    import numpy as np
+
+    from oracle import paged_attention as O
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from plan_oracle import run_oracle
+
+    kp, vp, _, _ = run_oracle(wl, wl.setup + [op for op in wl.step if op[0] != "decode"])
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas = None
+    done = 0
+    kv = 0
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    while done < wl.num_seqs and (done == 0 or time.perf_counter() - t0 < budget_s):
+        O.decode_attention(wl.q, kp, vp, wl.tables["final"], wl.context_lens, wl.scale, wl.dtype,
+                           seqs=[done])
+        kv += int(wl.context_lens[done]) * wl.num_kv_heads * wl.head_dim * 2 * (2 if wl.dtype == "bf16" else 4)
+        done += 1
+    wall = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    return {
+        "value": kv / wall / 1e9, "unit": "GB/s", "cores": round(cpu / wall, 2), "kind": "oracle",
+        "sample": (f"float64 numpy oracle decode of the first {done} of {wl.num_seqs} sequences "
+                   f"(all {wl.num_q_heads} query heads) of the same workload: {wall:.1f} s wall, "
+                   f"{done / wall:.2f} seq-steps/s; cores = CPU time / wall time; "
+                   f"BLAS pool {blas} threads; host affinity {len(os.sched_getaffinity(0))} cpus"),
+        "seq_steps_per_s": done / wall,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each sequence's blocks live on one GPU; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    import paged_kv_cache_188_amd as pa
+    import workloads as W
+    from workloads.device import DeviceWorkload
+
+    wl = W.make(args.config)
+    dev = DeviceWorkload(wl)
+    dev.run_setup()
+    dev.release_setup_inputs()
+    pool_bytes = 2 * dev.pools[0][0].numel() * dev.pools[0][0].element_size()
+    npools = max(2, min(8, -(-4 * LLC_BYTES // pool_bytes) + 1))
+    dev.add_pool_copies(npools - 1)
+    torch.cuda.synchronize()
+
+    decode_ops = [op for op in dev.step_ops if op[0] == "decode"]
+    other_ops = [op for op in dev.step_ops if op[0] != "decode"]
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        pool = k % npools
+        dev._run(other_ops, pool)
+        if ev is not None:
+            ev[0].record(stream)
+        dev._run(decode_ops, pool)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in events]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    kv_bytes = wl.kv_bytes_read()
+    dec_bytes = wl.decode_bytes()
+    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+            "block_size": wl.block_size, "num_blocks": wl.num_blocks,
+            "sum_context_tokens": int(wl.context_lens.sum()),
+            "max_context_len": wl.max_context_len,
+            "partition_size": pa.decode_partition_size(wl.num_seqs, wl.num_kv_heads,
+                                                       wl.block_size, wl.max_context_len,
+                                                       wl.partition_size),
+            "seed": list(wl.seed), "pool_copies_rotated": npools,
+            "parallelism": "single GPU",
+        },
+        "seq_steps_per_s": round(wl.num_seqs / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_ms": {"avg": round(dec_avg_ms, 5), "min": round(min(dec_ms), 5),
+                      "max": round(max(dec_ms), 5)},
+        "roofline": {
+            "kernel": "pa_decode_attention (decode kernel + partition merge)",
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": dec_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

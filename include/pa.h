@@ -1,0 +1,212 @@
+/*
+ * pa.h -- paged KV cache hot path for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels for the three GPU operations of
+ * PagedAttention's decode step:
+ *
+ *   pa_compute_slots     logical (sequence, position) -> physical cache slot
+ *   pa_write_kv          store new tokens' K/V in their slots
+ *   pa_copy_blocks       copy whole KV blocks (copy-on-write of shared blocks)
+ *   pa_decode_attention  one query token per sequence attends to its history,
+ *                        reached block by block through its block table
+ *
+ * Sources, cited by page title and section:
+ *   [nalar]    "PagedAttention: memetakan blok KV logis ke memori fisik tidak
+ *              kontigu" (nalar.dev)
+ *   [bicarait] "Melihat Lebih Dalam vLLM v0.7: Bagaimana PagedAttention &
+ *              Chunked Prefill ..." (bicarait.com)
+ *   [gininih]  "Apa itu PagedAttention (Manajemen Memori KV Cache GPU)?"
+ *              (gininih.com)
+ *   [gyaansetu] "KV Cache and PagedAttention: Why Your LLM Server Slows Down"
+ *              (gyaansetu.com)
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every entry point
+ * ---------------------------------------------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer on the current HIP
+ *   device.  The caller allocates and owns all memory, including the decode
+ *   workspace; the library allocates nothing and keeps no pointer after the
+ *   call returns.  Pools are updated in place.
+ * Streams.  `stream` is a hipStream_t passed as void*; NULL is the null
+ *   stream.  Every call only enqueues work and returns; results are visible
+ *   in stream order.  Ordering between calls (write -> attend, copy -> attend)
+ *   is the caller's stream order.
+ * Element types.  PA_F32 (IEEE binary32) or PA_BF16 (bfloat16, the upper
+ *   16 bits of a binary32).  K, V, new K/V and Q share one element type.
+ * Layouts (row-major, contiguous):
+ *   k_cache, v_cache   [num_blocks][num_kv_heads][block_size][head_dim]
+ *                      -- one (block, KV head) chunk is block_size*head_dim
+ *                      contiguous elements
+ *   block_tables       int32 [num_seqs][max_blocks_per_seq]; entry b is the
+ *                      physical block of logical block b; entries past the
+ *                      last used block are never read (may hold -1)
+ *   context_lens       int32 [num_seqs]
+ *   q                  [num_seqs][num_q_heads][head_dim]
+ *   out                float32 [num_seqs][num_q_heads][head_dim]
+ *   k_new, v_new       [num_tokens][num_kv_heads][head_dim] with a token
+ *                      stride (in elements) that may exceed num_kv_heads*head_dim
+ *   slot_mapping       int64 [num_tokens]; -1 = padding token (skipped)
+ *   block_mapping      int32 [num_pairs][2] = (src, dst)
+ * Errors.  Scalar arguments are validated on the host before any HIP call,
+ *   so a rejected call has no effect and is safe without a GPU.  The contents
+ *   of device arrays are not validated (that would need a synchronisation);
+ *   instead every kernel bounds-checks each index it reads from device memory
+ *   (slot, block id, sequence id, context length) and skips or clamps an
+ *   access that would leave its buffer, so a bad table cannot make the GPU
+ *   fault; the affected results are then unspecified.  A launch failure is
+ *   reported as PA_ERR_HIP.
+ * Threading.  No mutable global state; concurrent calls on different streams
+ *   are safe when their output buffers are disjoint.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,         /* a required pointer is NULL                     */
+  PA_ERR_SHAPE = 2,        /* a size is out of range or sizes disagree       */
+  PA_ERR_DTYPE = 3,        /* unknown element type                           */
+  PA_ERR_UNSUPPORTED = 4,  /* head_dim, block_size or partition not supported*/
+  PA_ERR_WORKSPACE = 5,    /* decode workspace missing or too small          */
+  PA_ERR_HIP = 6           /* the HIP runtime reported an error              */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Supported shapes (checked by every entry point):
+ *   head_dim   in {64, 128}
+ *   block_size in {8, 16, 32, 64}
+ *   num_q_heads a multiple of num_kv_heads, num_q_heads/num_kv_heads <= 16   */
+
+/* ---------------------------------------------------------------------------
+ * pa_compute_slots
+ *
+ * [nalar] "Urutan logis dipisahkan dari penempatan fisik" and [bicarait]
+ * "Blueprint Arsitektur 2": a sequence's logical block b lives in physical
+ * block block_tables[seq][b]; tokens keep their logical order inside a block.
+ * For token j:
+ *     p = positions[j], i = seq_ids[j]
+ *     slots[j] = block_tables[i][p / block_size] * block_size + p % block_size
+ * computed in 64-bit integers.  slots[j] = -1 when p < 0 (padding), and also
+ * when i is not in [0, num_seqs), p / block_size >= max_blocks_per_seq, or the
+ * table entry is not in [0, num_blocks) -- such a token is then skipped by
+ * pa_write_kv.  seq_ids may be NULL: token j then belongs to sequence j
+ * (one new token per sequence, the decode step).
+ * ------------------------------------------------------------------------- */
+pa_status pa_compute_slots(int64_t* slots, const int32_t* block_tables,
+                           int32_t num_seqs, int32_t max_blocks_per_seq,
+                           const int32_t* seq_ids, const int32_t* positions,
+                           int32_t num_tokens, int32_t block_size,
+                           int32_t num_blocks, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_write_kv  (reshape-and-cache)
+ *
+ * [gyaansetu] "Apa itu KV Cache?": only the new token's K and V are computed;
+ * they are stored so later steps read them back.  For each token j with
+ * 0 <= slot_mapping[j] < num_blocks*block_size, and each KV head h:
+ *     k_cache[slot / block_size][h][slot % block_size][:] = k_new[j][h][:]
+ *     v_cache[...same...]                                 = v_new[j][h][:]
+ * A bit copy (exact).  Negative slots and slots beyond the pool are skipped.
+ * Two tokens with the same slot race (caller error).  new_token_stride is
+ * the distance in elements between consecutive tokens of k_new and v_new;
+ * 0 means num_kv_heads*head_dim.  It must be a multiple of 8 elements for
+ * bf16 and 4 for f32 (16-byte rows), and the pointers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new,
+                      const void* v_new, const int64_t* slot_mapping,
+                      int32_t num_tokens, int64_t new_token_stride,
+                      int32_t num_blocks, int32_t block_size,
+                      int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_copy_blocks  (copy-on-write)
+ *
+ * [nalar] "Sharing blok dapat menghindari duplikasi state KV" and [gininih]
+ * "Cara kerja PagedAttention": a branch that must modify a shared block gets
+ * its own physical copy.  For each pair n: block dst = block_mapping[n][1]
+ * receives every KV head of block src = block_mapping[n][0], in both pools
+ * (one layer per call).  Bit copy.  Pairs naming a block outside
+ * [0, num_blocks) are skipped.  Destinations must be distinct and must not be
+ * sources of the same call (otherwise the result depends on the order).
+ * ------------------------------------------------------------------------- */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache,
+                         const int32_t* block_mapping, int32_t num_pairs,
+                         int32_t num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         pa_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode_attention
+ *
+ * [nalar] "Kernel attention harus mengikuti block table": for each sequence's
+ * query token the kernel walks the logical context in order and translates
+ * each logical block to its physical block before loading K and V.  [nalar]
+ * introduction and [gininih] "Batasan dan salah paham umum": the attention
+ * equation is unchanged.  For sequence i, query head h, and
+ * n = context_lens[i] (tokens 0..n-1 of its logical history):
+ *     g     = h / (num_q_heads / num_kv_heads)       (grouped-query heads)
+ *     s_t   = scale * dot(q[i][h], K_t[g])           t = 0..n-1
+ *     out[i][h] = sum_t softmax(s)_t * V_t[g]        (float32 result)
+ * where K_t / V_t is token t's row reached through block_tables[i].
+ * n == 0 gives zeros.  n is clamped to [0, max_blocks_per_seq*block_size].
+ * Scores, softmax and the weighted sum are accumulated in float32 from the
+ * exact float32 values of the stored elements.
+ *
+ * max_context_len is a host-side upper bound of every context_lens[i]; it
+ * sizes the grid and the workspace (a larger bound is correct, just slower).
+ * partition_size splits each context into partitions of that many tokens
+ * that are processed independently and merged with an exact log-sum-exp
+ * rescale; 0 lets the library choose (pa_decode_partition_size).  A nonzero
+ * value must be a multiple of 16 and of block_size.  The workspace (float32
+ * partial maxima, sums and outputs) must hold pa_decode_workspace_size()
+ * bytes for the same arguments; it may be NULL when that size is 0.
+ * flags: 0, or PA_DECODE_VECTOR_ONLY to run the plain vector-ALU kernel
+ * instead of the matrix-core kernel (both give results within the same
+ * tolerance; the flag exists for cross-checking).
+ * The result is deterministic: it depends on the logical contents and the
+ * partitioning only, never on physical block ids or on timing.
+ * ------------------------------------------------------------------------- */
+#define PA_DECODE_VECTOR_ONLY 1u
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                 int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size);
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_context_len,
+                                int32_t partition_size);
+
+pa_status pa_decode_attention(float* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale,
+                              int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, pa_dtype dtype,
+                              uint32_t flags, void* stream);
+
+/* Text of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -207,7 +207,7 @@ def _kv_head(q_head: int, group: int) -> int:
 
 def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                      block_tables: np.ndarray, context_lens: np.ndarray,
-                     scale: float, dtype: str) -> np.ndarray:
+                     scale: float, dtype: str, seqs=None, heads=None) -> np.ndarray:
     """Exact softmax attention of one query token per sequence, float64.
 
     [nalar] "Kernel attention harus mengikuti block table": for the query, walk
@@ -221,6 +221,10 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     q is ``[S][Hq][D]``; pools ``[NB][Hkv][bs][D]``; the table ``[S][MB]``
     (entries past the last used block are never read).  Returns
     ``[S][Hq][D]`` float64; a sequence with ``ctx == 0`` gets zeros.
+
+    ``seqs`` / ``heads`` (optional index lists) restrict the work to those
+    sequences and query heads, for checking samples of a large batch; rows not
+    computed are NaN.
     """
     num_seqs, num_q_heads, head_dim = q.shape
     num_blocks, num_kv_heads, block_size, head_dim_kv = k_pool.shape
@@ -234,11 +238,16 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     scale64 = np.float64(np.float32(scale))
     q64 = to_f64(q, dtype)
     out = np.zeros((num_seqs, num_q_heads, head_dim), dtype=np.float64)
-    for i in range(num_seqs):
+    if seqs is not None or heads is not None:
+        out[:] = np.nan
+    seq_list = range(num_seqs) if seqs is None else [int(i) for i in seqs]
+    head_list = range(num_q_heads) if heads is None else [int(h) for h in heads]
+    for i in seq_list:
         n = int(ctx[i])
         if n < 0 or n > bt.shape[1] * block_size:
             raise ContractError(f"sequence {i}: context length {n} outside the table")
         if n == 0:
+            out[i, list(head_list)] = 0.0
             continue
         t = np.arange(n)
         lb = np.array([_logical_block(int(p), block_size) for p in t])
@@ -246,7 +255,7 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         phys = bt[i, lb]
         if phys.min() < 0 or phys.max() >= num_blocks:
             raise ContractError(f"sequence {i}: table entry is not a pool block")
-        for h in range(num_q_heads):
+        for h in head_list:
             g = _kv_head(h, group)
             k_t = to_f64(k_pool[phys, g, off, :], dtype)        # [n][D]
             v_t = to_f64(v_pool[phys, g, off, :], dtype)        # [n][D]

@@ -1,0 +1,190 @@
+// C ABI of libpa: argument validation, launch configuration, workspace sizing
+// and error mapping.  Validation touches scalars and pointer values only and
+// runs before any HIP call, so a rejected call has no effect.
+
+#include <cmath>
+#include <cstdint>
+
+#include "pa_internal.h"
+
+namespace {
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+bool supported_block_size(int32_t bs) { return bs == 8 || bs == 16 || bs == 32 || bs == 64; }
+bool valid_dtype(pa_dtype t) { return t == PA_F32 || t == PA_BF16; }
+int elem_bytes(pa_dtype t) { return t == PA_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// A partition is a whole number of 16-token tiles and of blocks, at most 64
+// blocks (the decode kernel keeps one block id per lane).
+bool valid_partition(int32_t part, int32_t bs) {
+  return part > 0 && part % 16 == 0 && part % bs == 0 && part / bs <= 64;
+}
+
+// Library choice: start from the largest allowed partition (<= 1024 tokens)
+// and halve while the grid would hold fewer than kTargetItems work items --
+// enough independent waves to fill 256 CUs with several waves each -- but not
+// below max(64, tile, block).
+constexpr int64_t kTargetItems = 4096;
+
+int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t bs, int32_t max_ctx) {
+  const int32_t unit = bs > 16 ? bs : 16;
+  int32_t part = 64 * bs < 1024 ? 64 * bs : 1024;
+  part -= part % unit;
+  const int32_t floor_part = unit > 64 ? unit : 64;
+  auto items = [&](int32_t pt) {
+    const int64_t p = max_ctx > 0 ? (max_ctx + (int64_t)pt - 1) / pt : 1;
+    return (int64_t)num_seqs * num_kv_heads * p;
+  };
+  while (part / 2 >= floor_part && (part / 2) % unit == 0 && items(part) < kTargetItems) part /= 2;
+  return part;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case PA_ERR_DTYPE: return "unknown element type";
+    case PA_ERR_UNSUPPORTED: return "head_dim, block_size, partition or alignment not supported";
+    case PA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+pa_status pa_compute_slots(int64_t* slots, const int32_t* block_tables, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, const int32_t* seq_ids,
+                           const int32_t* positions, int32_t num_tokens, int32_t block_size,
+                           int32_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1)
+    return PA_ERR_SHAPE;
+  if (!supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!slots || !positions || (num_seqs > 0 && !block_tables)) return PA_ERR_NULL;
+  return from_hip(pa::launch_compute_slots(slots, block_tables, num_seqs, max_blocks_per_seq,
+                                           seq_ids, positions, num_tokens, block_size, num_blocks,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int32_t num_tokens, int64_t new_token_stride,
+                      int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                      int32_t head_dim, pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks < 1 || num_kv_heads < 1) return PA_ERR_SHAPE;
+  if (!supported_block_size(block_size) || !supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (new_token_stride == 0) new_token_stride = row;
+  if (new_token_stride < row) return PA_ERR_SHAPE;
+  const int e = elem_bytes(dtype);
+  if ((new_token_stride * e) % 16) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return PA_ERR_UNSUPPORTED;
+  return from_hip(pa::launch_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
+                                      new_token_stride * e, num_blocks, block_size, num_kv_heads,
+                                      head_dim * e, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                         int32_t num_pairs, int32_t num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_pairs < 0 || num_blocks < 1 || num_kv_heads < 1) return PA_ERR_SHAPE;
+  if (!supported_block_size(block_size) || !supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_blocks,
+                                         block_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (!supported_block_size(block_size) || num_seqs < 0 || num_kv_heads < 1 || max_context_len < 0)
+    return 0;
+  if (partition_size != 0) return valid_partition(partition_size, block_size) ? partition_size : 0;
+  return choose_partition(num_seqs, num_kv_heads, block_size, max_context_len);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                int32_t partition_size) {
+  if (num_q_heads < 1 || !supported_head_dim(head_dim)) return 0;
+  const int32_t part = pa_decode_partition_size(num_seqs, num_kv_heads, block_size,
+                                                max_context_len, partition_size);
+  if (part <= 0) return 0;
+  const int64_t P = max_context_len > 0 ? (max_context_len + (int64_t)part - 1) / part : 1;
+  return pa::decode_workspace(num_seqs, num_q_heads, head_dim, (int)P).total;
+}
+
+pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                              int32_t partition_size, void* workspace, size_t workspace_bytes,
+                              pa_dtype dtype, uint32_t flags, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1 || max_context_len < 0 || num_q_heads % num_kv_heads)
+    return PA_ERR_SHAPE;
+  if (num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if (flags & ~PA_DECODE_VECTOR_ONLY) return PA_ERR_UNSUPPORTED;
+  if (partition_size != 0 && !valid_partition(partition_size, block_size)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  const int32_t max_tokens = max_blocks_per_seq * block_size;
+  // Same partition and partition count as pa_decode_workspace_size.
+  const int32_t part = partition_size ? partition_size
+                                      : choose_partition(num_seqs, num_kv_heads, block_size,
+                                                         max_context_len);
+  const int64_t P = max_context_len > 0 ? (max_context_len + (int64_t)part - 1) / part : 1;
+  if ((int64_t)num_seqs * num_kv_heads * P / 4 >= INT32_MAX) return PA_ERR_SHAPE;
+  const pa::DecodeWorkspace ws = pa::decode_workspace(num_seqs, num_q_heads, head_dim, (int)P);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PA_ERR_WORKSPACE;
+  if (ws.total > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+
+  pa::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  char* wsb = static_cast<char*>(workspace);
+  p.ws_m = ws.total ? reinterpret_cast<float*>(wsb + ws.m_off) : nullptr;
+  p.ws_l = ws.total ? reinterpret_cast<float*>(wsb + ws.l_off) : nullptr;
+  p.ws_acc = ws.total ? reinterpret_cast<float*>(wsb + ws.acc_off) : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.partition = part;
+  p.max_partitions = (int)P;
+  p.max_tokens = (int)((int64_t)P * part < max_tokens ? (int64_t)P * part : max_tokens);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(pa::launch_decode(p, head_dim, block_size, dtype,
+                                    (flags & PA_DECODE_VECTOR_ONLY) != 0,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Slot computation, slot-mapped KV write and copy-on-write block copy for gfx950.
+//
+// These three operations move or index data only; they are bit-exact.
+//
+//  * Slots follow the block table of [nalar] "Urutan logis dipisahkan dari
+//    penempatan fisik": logical block b of a sequence lives in physical block
+//    table[b]; a token keeps its logical order inside its block.
+//  * The write stores only the new tokens' K/V ([gyaansetu] "Apa itu KV
+//    Cache?").  Pool layout [NB][Hkv][bs][D]: one token of one KV head is a
+//    D-element row, so a token scatters Hkv rows of D*e bytes (256 B for bf16,
+//    D=128), each written with full 16-byte stores.
+//  * The block copy gives a diverging branch its own copy of a shared block
+//    ([nalar] "Sharing blok dapat menghindari duplikasi state KV"); a block is
+//    Hkv*bs*D*e contiguous bytes in each pool, streamed with 16-byte loads.
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+__global__ __launch_bounds__(256) void compute_slots_kernel(
+    int64_t* __restrict__ slots, const int32_t* __restrict__ block_tables, int num_seqs,
+    int max_blocks_per_seq, const int32_t* __restrict__ seq_ids,
+    const int32_t* __restrict__ positions, int num_tokens, int block_size, int num_blocks) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= num_tokens) return;
+  const int p = positions[j];
+  const int i = seq_ids ? seq_ids[j] : j;
+  int64_t slot = -1;
+  if (p >= 0 && i >= 0 && i < num_seqs) {
+    const int b = p / block_size;
+    if (b < max_blocks_per_seq) {
+      const int phys = block_tables[(int64_t)i * max_blocks_per_seq + b];
+      if (phys >= 0 && phys < num_blocks)
+        slot = (int64_t)phys * block_size + (p - b * block_size);
+    }
+  }
+  slots[j] = slot;
+}
+
+// One wave per token; each lane moves 16-byte chunks of the token's
+// [Hkv][D] row into the Hkv scattered rows of its slot.
+constexpr int kWriteWaves = 4;
+
+__global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int64_t token_stride_bytes,
+    int64_t pool_slots, int block_size, int num_kv_heads, int head_chunks) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int j = blockIdx.x * kWriteWaves + wave;
+  if (j >= num_tokens) return;
+  const int64_t slot = slot_mapping[j];
+  if (slot < 0 || slot >= pool_slots) return;  // padding token, or outside the pool
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int nchunks = num_kv_heads * head_chunks;
+  const uint8_t* ksrc = k_new + (int64_t)j * token_stride_bytes;
+  const uint8_t* vsrc = v_new + (int64_t)j * token_stride_bytes;
+  for (int c = lane; c < nchunks; c += kWave) {
+    const int h = c / head_chunks;
+    const int w = c - h * head_chunks;
+    const int64_t dst = (((blk * num_kv_heads + h) * block_size + off) * head_chunks + w) * 16;
+    const uint4 a = *reinterpret_cast<const uint4*>(ksrc + (int64_t)c * 16);
+    const uint4 b = *reinterpret_cast<const uint4*>(vsrc + (int64_t)c * 16);
+    *reinterpret_cast<uint4*>(k_cache + dst) = a;
+    *reinterpret_cast<uint4*>(v_cache + dst) = b;
+  }
+}
+
+// grid = (pair, pool K/V, 16 KiB piece of the block).  Each thread moves up
+// to four 16-byte chunks, all loads issued before the stores.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+constexpr int64_t kCopyPieceBytes = (int64_t)kCopyThreads * kCopyUnroll * 16;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const int32_t* __restrict__ block_mapping, int num_blocks, int64_t block_bytes) {
+  const int pair = blockIdx.x;
+  const int src = block_mapping[2 * pair];
+  const int dst = block_mapping[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint8_t* base = blockIdx.y ? v_cache : k_cache;
+  const uint4* s = reinterpret_cast<const uint4*>(base + (int64_t)src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>(base + (int64_t)dst * block_bytes);
+  const int64_t n = block_bytes / 16;
+  const int64_t first = (int64_t)blockIdx.z * (kCopyPieceBytes / 16) + threadIdx.x;
+  uint4 r[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = first + (int64_t)u * kCopyThreads;
+    if (i < n) r[u] = s[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = first + (int64_t)u * kCopyThreads;
+    if (i < n) d[i] = r[u];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compute_slots(int64_t* slots, const int32_t* block_tables, int num_seqs,
+                                int max_blocks_per_seq, const int32_t* seq_ids,
+                                const int32_t* positions, int num_tokens, int block_size,
+                                int num_blocks, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int threads = 256;
+  const int grid = (num_tokens + threads - 1) / threads;
+  hipLaunchKernelGGL(compute_slots_kernel, dim3(grid), dim3(threads), 0, stream, slots,
+                     block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions, num_tokens,
+                     block_size, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int num_tokens, int64_t token_stride_bytes,
+                           int num_blocks, int block_size, int num_kv_heads, int head_bytes,
+                           hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int grid = (num_tokens + kWriteWaves - 1) / kWriteWaves;
+  hipLaunchKernelGGL(write_kv_kernel, dim3(grid), dim3(kWriteWaves * kWave), 0, stream,
+                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                     static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
+                     slot_mapping, num_tokens, token_stride_bytes,
+                     (int64_t)num_blocks * block_size, block_size, num_kv_heads, head_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                              int num_pairs, int num_blocks, int64_t block_bytes,
+                              hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int pieces = (int)((block_bytes + kCopyPieceBytes - 1) / kCopyPieceBytes);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2, pieces), dim3(kCopyThreads), 0,
+                     stream, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                     block_mapping, num_blocks, block_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace pa

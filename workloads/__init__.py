@@ -16,8 +16,10 @@ pair through the named block table, then store K/V there -- or
 block the plan never writes stays poisoned; table padding is -1.
 
 Random draws: ``numpy.random.default_rng(SeedSequence([188, config_id]))``,
-drawn in the fixed order context lengths -> block permutation -> Q -> history
-K -> history V -> new-token K -> new-token V.  float32 draws are rounded to
+drawn in the fixed order context lengths -> block permutation -> Q ->
+new-token K -> new-token V; the (large) history K and V come from child
+seeds of ``SeedSequence([188, config_id, stream, 0 or 1])``, one per
+32768-token chunk.  float32 draws are rounded to
 bfloat16 by round-to-nearest-even once, here, so both sides see the same bits.
 """
 
@@ -164,15 +166,34 @@ def _positions(lengths, starts=None):
     return seq_ids, pos
 
 
-def _history_kv(rng, n_tokens, num_kv_heads, head_dim, dtype, chunk_tokens=1 << 17):
-    """Draw history K then V in token chunks (bounded float32 temporaries)."""
+HISTORY_CHUNK_TOKENS = 1 << 15
+
+
+def _history_kv(seed, stream_id, n_tokens, num_kv_heads, head_dim, dtype):
+    """History K then V for ``n_tokens`` tokens.
+
+    Token chunk c of K (V) is drawn from child c of
+    ``SeedSequence([*seed, stream_id, 0 (K) / 1 (V)])``, so the values do not
+    depend on how many threads draw them; chunks are drawn in parallel."""
+    import concurrent.futures as cf
+    import os
+    workers = max(1, min(16, os.cpu_count() or 1))
     out = []
-    for _ in range(2):
+    for which in range(2):
         buf = np.empty((n_tokens, num_kv_heads, head_dim),
                        dtype=np.uint16 if dtype == BF16 else np.float32)
-        for s in range(0, n_tokens, chunk_tokens):
-            e = min(n_tokens, s + chunk_tokens)
-            buf[s:e] = draw_normal(rng, (e - s, num_kv_heads, head_dim), dtype)
+        n_chunks = -(-n_tokens // HISTORY_CHUNK_TOKENS)
+        children = np.random.SeedSequence([*seed, stream_id, which]).spawn(n_chunks)
+
+        def fill(c, buf=buf, children=children):
+            s = c * HISTORY_CHUNK_TOKENS
+            e = min(n_tokens, s + HISTORY_CHUNK_TOKENS)
+            buf[s:e] = draw_normal(np.random.default_rng(children[c]),
+                                   (e - s, num_kv_heads, head_dim), dtype)
+
+        if n_chunks:
+            with cf.ThreadPoolExecutor(max_workers=min(workers, n_chunks)) as ex:
+                list(ex.map(fill, range(n_chunks)))
         out.append(buf)
     return out[0], out[1]
 
@@ -191,6 +212,8 @@ def decode_workload(name, dtype, ctx_lens, num_q_heads, num_kv_heads, head_dim,
     no token and no block."""
     ctx = np.asarray(ctx_lens, dtype=np.int32)
     S = ctx.size
+    if not seed:
+        seed = tuple(int(x) for x in rng.integers(0, 2**31 - 1, size=2))
     need_each = np.array([_blocks_for(int(c), block_size) for c in ctx], dtype=np.int64)
     need = int(need_each.sum())
     if num_blocks is None:
@@ -207,7 +230,7 @@ def decode_workload(name, dtype, ctx_lens, num_q_heads, num_kv_heads, head_dim,
         cursor += n
     q = draw_normal(rng, (S, num_q_heads, head_dim), dtype)
     hist_len = np.maximum(ctx.astype(np.int64) - 1, 0)
-    hk, hv = _history_kv(rng, int(hist_len.sum()), num_kv_heads, head_dim, dtype)
+    hk, hv = _history_kv(seed, 1, int(hist_len.sum()), num_kv_heads, head_dim, dtype)
     hs, hp = _positions(hist_len)
     has_new = ctx > 0
     new_seq = np.nonzero(has_new)[0].astype(np.int32)
@@ -248,6 +271,8 @@ def shared_prefix_workload(name, *, rng, seed=(), groups=32, samples=8, prefix=2
     the first tail tokens then land in the private copy and the copy-on-write
     is observable."""
     S = groups * samples
+    if not seed:
+        seed = tuple(int(x) for x in rng.integers(0, 2**31 - 1, size=2))
     tails = rng.integers(tail_lo, tail_hi, size=S, endpoint=True).astype(np.int64)
     ctx = (prefix + tails).astype(np.int32)
     n_prefix_blocks = _blocks_for(prefix, block_size)
@@ -284,9 +309,9 @@ def shared_prefix_workload(name, *, rng, seed=(), groups=32, samples=8, prefix=2
             fin[i, n_prefix_blocks:n_prefix_blocks + nt] = take(nt)
             pre[i, n_prefix_blocks:n_prefix_blocks + nt] = fin[i, n_prefix_blocks:n_prefix_blocks + nt]
     q = draw_normal(rng, (S, num_q_heads, head_dim), dtype)
-    pk, pv = _history_kv(rng, groups * prefix, num_kv_heads, head_dim, dtype)
+    pk, pv = _history_kv(seed, 1, groups * prefix, num_kv_heads, head_dim, dtype)
     tail_hist = tails - 1                       # the last token is the step's
-    tk, tv = _history_kv(rng, int(tail_hist.sum()), num_kv_heads, head_dim, dtype)
+    tk, tv = _history_kv(seed, 2, int(tail_hist.sum()), num_kv_heads, head_dim, dtype)
     nk = draw_normal(rng, (S, num_kv_heads, head_dim), dtype)
     nv = draw_normal(rng, (S, num_kv_heads, head_dim), dtype)
     ps, pp = _positions(np.full(groups, prefix))

@@ -1,0 +1,122 @@
+"""Execute a workload plan on the GPU through the libpa binding.
+
+Uploads the generated arrays (element bits unchanged), allocates every
+buffer the plan needs up front, and runs the setup ops once and the step ops
+on demand.  It performs no arithmetic of the method itself: slots, writes,
+copies and attention all run in libpa's kernels.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import paged_kv_cache_188_amd as pa
+
+from . import BF16, Workload
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(arr)
+    if dtype == BF16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a.view(np.float32)).to(device)
+
+
+def to_host_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
+    if dtype == BF16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class DeviceWorkload:
+    """Device buffers of one workload and its plan."""
+
+    def __init__(self, wl: Workload, device="cuda"):
+        self.wl = wl
+        self.device = device
+        kp, vp = wl.empty_pools()
+        self.pools = [(to_device(kp, wl.dtype, device), to_device(vp, wl.dtype, device))]
+        del kp, vp
+        self.q = to_device(wl.q, wl.dtype, device)
+        self.tables = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device)
+                       for k, v in wl.tables.items()}
+        self.ctx = torch.from_numpy(np.ascontiguousarray(wl.context_lens)).to(device)
+        self.out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32,
+                               device=device)
+        self.max_ctx = wl.max_context_len
+        need = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
+                                        wl.head_dim, wl.block_size, self.max_ctx,
+                                        wl.partition_size)
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        self.setup_ops = [self._upload(op) for op in wl.setup]
+        self.step_ops = [self._upload(op) for op in wl.step]
+
+    def _upload(self, op):
+        kind, x = op
+        if kind == "write":
+            return ("write", dict(
+                table=x.table,
+                seq_ids=torch.from_numpy(np.ascontiguousarray(x.seq_ids)).to(self.device),
+                positions=torch.from_numpy(np.ascontiguousarray(x.positions)).to(self.device),
+                k=to_device(x.k, self.wl.dtype, self.device),
+                v=to_device(x.v, self.wl.dtype, self.device),
+                slots=torch.empty(x.positions.size, dtype=torch.int64, device=self.device)))
+        if kind == "copy":
+            return ("copy", torch.from_numpy(np.ascontiguousarray(x)).to(self.device))
+        if kind == "decode":
+            return ("decode", x)
+        raise ValueError(kind)
+
+    # -------------------------------------------------------------------
+    def _run(self, ops, pool=0, partition_size=None, vector_only=False, stream=None):
+        wl = self.wl
+        k, v = self.pools[pool]
+        part = wl.partition_size if partition_size is None else partition_size
+        for kind, x in ops:
+            if kind == "write":
+                pa.compute_slots(self.tables[x["table"]], x["positions"], wl.block_size,
+                                 wl.num_blocks, seq_ids=x["seq_ids"], out=x["slots"],
+                                 stream=stream)
+                pa.write_kv(k, v, x["k"], x["v"], x["slots"], stream=stream)
+            elif kind == "copy":
+                pa.copy_blocks(k, v, x, stream=stream)
+            else:
+                ws = self.workspace
+                if part != wl.partition_size:
+                    need = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
+                                                    wl.head_dim, wl.block_size, self.max_ctx, part)
+                    if need > ws.numel():
+                        ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+                pa.decode_attention(self.q, k, v, self.tables[x], self.ctx, wl.scale, self.max_ctx,
+                                    partition_size=part, workspace=ws, out=self.out,
+                                    vector_only=vector_only, stream=stream)
+        return self.out
+
+    def run_setup(self, pool=0):
+        self._run(self.setup_ops, pool)
+
+    def run_step(self, pool=0, **kw):
+        return self._run(self.step_ops, pool, **kw)
+
+    def decode_only(self, pool=0, **kw):
+        return self._run([op for op in self.step_ops if op[0] == "decode"], pool, **kw)
+
+    def release_setup_inputs(self):
+        """Drop the uploaded history (only the setup ops need it)."""
+        self.setup_ops = []
+        torch.cuda.empty_cache()
+
+    def add_pool_copies(self, n: int):
+        """n more independent pool pairs with the current contents (for timing
+        without cache reuse between steps)."""
+        k, v = self.pools[0]
+        for _ in range(n):
+            self.pools.append((k.clone(), v.clone()))
+
+    def slots_of(self, ops):
+        return [x["slots"].cpu().numpy() for kind, x in ops if kind == "write"]
+
+    def pool_bits(self, pool=0):
+        k, v = self.pools[pool]
+        return to_host_bits(k, self.wl.dtype), to_host_bits(v, self.wl.dtype)
