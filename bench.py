@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="decode partition size (default: the workload's / the library's choice)")
     return ap.parse_args()
 
 
@@ -102,6 +104,8 @@ def main():
     from workloads.device import DeviceWorkload
 
     wl = W.make(args.config)
+    if args.partition is not None:
+        wl.partition_size = args.partition
     dev = DeviceWorkload(wl)
     dev.run_setup()
     dev.release_setup_inputs()

@@ -143,11 +143,11 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
     t = slot_mapping.numel()
     if k_new.shape[0] != t or v_new.shape != k_new.shape or tuple(k_new.shape[1:]) != (hkv, d):
         raise ValueError("k_new/v_new must be [T][Hkv][D] matching slot_mapping")
-    if k_new.stride(2) != 1 or k_new.stride(1) != d or v_new.stride() != k_new.stride():
+    if t and (k_new.stride(2) != 1 or k_new.stride(1) != d or v_new.stride() != k_new.stride()):
         raise ValueError("k_new/v_new rows must be contiguous [Hkv][D] with one token stride")
     _check("pa_write_kv", lib().pa_write_kv(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), t,
-        k_new.stride(0), nb, bs, hkv, d, _dtype_code(k_cache), _stream(stream)))
+        k_new.stride(0) if t else 0, nb, bs, hkv, d, _dtype_code(k_cache), _stream(stream)))
 
 
 def copy_blocks(k_cache, v_cache, block_mapping, stream=None):

@@ -49,6 +49,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kDecodeWaves = 4;  // independent work items per workgroup
+constexpr int kRing = 4;         // 16-token tiles held in registers per wave (3 in flight)
+constexpr float kLazyMax = 8.f;  // headroom (log2) before the running max must move
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -86,11 +88,15 @@ __device__ __forceinline__ bool decode_item(const DecodeParams& p, int64_t item,
 // ---------------------------------------------------------------------------
 
 template <int D, int BS>
-__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(const DecodeParams p) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KSTEPS = D / 32;  // QK k-steps
   constexpr int DV = D / 16;      // V dims per lane per row == PV n-tiles
   using VRow = typename std::conditional<DV == 8, uint4, uint2>::type;
+  struct Tile {
+    uint4 k[KSTEPS];  // key row `col`, dims 32*s + 8*grp .. +7
+    VRow v[4];        // value rows 4*grp + j, dims DV*col .. +DV-1
+  };
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -126,26 +132,28 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_mfma_kernel(const
   const uint16_t* kpool = static_cast<const uint16_t*>(p.k_cache);
   const uint16_t* vpool = static_cast<const uint16_t*>(p.v_cache);
   const int64_t chunk = (int64_t)BS * D;  // elements of one (block, KV head) chunk
-
   auto chunk_base = [&](int phys) -> int64_t {
     return ((int64_t)phys * p.num_kv_heads + it.kvh) * chunk;
   };
-  uint4 kr[KSTEPS];
-  VRow vr[4];
-  // Tile tb covers tokens tb..tb+15 (tb a multiple of 16).  For BS >= 16 they
-  // lie in one block, whose id is wave-uniform (readlane); for BS == 8 a tile
-  // spans two blocks and each lane fetches its row's id with a lane shuffle.
-  // Rows past the partition's last block reuse its id (they are masked).
-  auto load_tile = [&](int tb, uint4 (&k)[KSTEPS], VRow (&v)[4]) {
+  const int ntiles = (it.end - it.start + 15) / 16;
+
+  // Tile t covers tokens start+16t .. +15.  For BS >= 16 they lie in one
+  // block, whose id is wave-uniform (readlane); for BS == 8 a tile spans two
+  // blocks and each lane fetches its row's id with a lane shuffle.  Rows past
+  // the partition's last block reuse its id (they are masked).  The index is
+  // clamped to the last tile, so the ring can be refilled unconditionally:
+  // loads past the end re-read the last tile (from cache) and are never used.
+  auto load = [&](int t, Tile& b) {
+    const int tb = it.start + 16 * min(t, ntiles - 1);
     if constexpr (BS >= 16) {
       const int phys = __builtin_amdgcn_readlane(my_id, tb / BS - b0);
       const int64_t cb = chunk_base(phys) + (int64_t)(tb % BS) * D;
       const uint16_t* kb = kpool + cb + (int64_t)col * D + 8 * grp;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) k[s] = *reinterpret_cast<const uint4*>(kb + 32 * s);
+      for (int s = 0; s < KSTEPS; ++s) b.k[s] = *reinterpret_cast<const uint4*>(kb + 32 * s);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        v[j] = *reinterpret_cast<const VRow*>(vpool + cb + (int64_t)(4 * grp + j) * D + DV * col);
+        b.v[j] = *reinterpret_cast<const VRow*>(vpool + cb + (int64_t)(4 * grp + j) * D + DV * col);
     } else {
       auto row_base = [&](int tok) -> int64_t {
         const int lb = min(tok / BS - b0, nblk - 1);
@@ -153,37 +161,30 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_mfma_kernel(const
       };
       const uint16_t* kb = kpool + row_base(tb + col) + 8 * grp;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) k[s] = *reinterpret_cast<const uint4*>(kb + 32 * s);
+      for (int s = 0; s < KSTEPS; ++s) b.k[s] = *reinterpret_cast<const uint4*>(kb + 32 * s);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        v[j] = *reinterpret_cast<const VRow*>(vpool + row_base(tb + 4 * grp + j) + DV * col);
+        b.v[j] = *reinterpret_cast<const VRow*>(vpool + row_base(tb + 4 * grp + j) + DV * col);
     }
   };
 
   f32x4_t acc[DV];
 #pragma unroll
   for (int nt = 0; nt < DV; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // m_run: reference point of the exponentials of head `col` (log2 domain).
+  // It is moved only when a score exceeds it by more than kLazyMax, so every
+  // weight 2^(x - m_run) stays <= 2^kLazyMax and the common path needs no
+  // cross-lane traffic; results are exact either way (partials carry m_run).
   float m_run = kNegInf;
   float l_run = 0.f;
 
-  const int ntiles = (it.end - it.start + 15) / 16;
-  if (ntiles > 0) load_tile(it.start, kr, vr);
-  for (int t = 0; t < ntiles; ++t) {
+  auto compute = [&](int t, Tile& b) {
     const int tb = it.start + 16 * t;
-    uint4 kc[KSTEPS];
-    VRow vc[4];
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) kc[s] = kr[s];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vc[j] = vr[j];
-    if (t + 1 < ntiles) load_tile(tb + 16, kr, vr);  // prefetch the next tile
-
     // scores: lane holds head `col`, tokens tb + 4*grp + i
     f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[s]), qv[s], sc, 0, 0, 0);
-
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(b.k[s]), qv[s], sc, 0, 0, 0);
     const bool full = tb + 16 <= it.end;
     float x[4];
 #pragma unroll
@@ -191,16 +192,13 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_mfma_kernel(const
       const bool ok = full || (tb + 4 * grp + i < it.end);
       x[i] = ok ? sc[i] * p.scale_log2 : kNegInf;
     }
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - m_new);
-    const float alpha = fast_exp2(m_run - m_new);
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    if (__any(m_new > m_run)) {
+    const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__any(lmax > m_run + kLazyMax)) {
+      float mt = fmaxf(lmax, __shfl_xor(lmax, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
+      l_run *= alpha;
       // rows of acc are heads 4*grp + r; their factor lives in lane 4*grp + r
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -208,21 +206,40 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_mfma_kernel(const
 #pragma unroll
         for (int nt = 0; nt < DV; ++nt) acc[nt][r] *= a;
       }
+      m_run = m_new;
     }
-    m_run = m_new;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - m_run);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     if (!full) {  // zero V rows past the end (they may hold anything, NaN included)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (tb + 4 * grp + j >= it.end) vc[j] = VRow{};
+        if (tb + 4 * grp + j >= it.end) b.v[j] = VRow{};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(&vc[j]);
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(&b.v[j]);
 #pragma unroll
       for (int nt = 0; nt < DV; ++nt) {
         const float v = (nt & 1) ? bf16_hi(w[nt >> 1]) : bf16_lo(w[nt >> 1]);
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[j], v, acc[nt], 0, 0, 0);
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    // The first pass only fills the ring, so every path into a compute has
+    // issued the ring's loads in the same order (the compiler can then wait
+    // for the oldest tile alone).
+    Tile ring[kRing];
+    for (int t0 = -kRing; t0 < ntiles; t0 += kRing) {
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        const int t = t0 + i;
+        if (t >= 0 && t < ntiles) compute(t, ring[i]);
+        load(t + kRing, ring[i]);
       }
     }
   }
@@ -239,15 +256,13 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_mfma_kernel(const
     const float m_h = __shfl(m_run, h);
     if (h >= G) continue;
     const int64_t row = (int64_t)it.seq * p.num_q_heads + hq0 + h;
-    float vals[DV];
     if (single) {
       const float inv = l_h > 0.f ? 1.0f / l_h : 0.f;
-#pragma unroll
-      for (int nt = 0; nt < DV; ++nt) vals[nt] = acc[nt][r] * inv;
       float* dst = p.out + row * D + DV * col;
 #pragma unroll
       for (int c = 0; c < DV; c += 4)
-        *reinterpret_cast<float4*>(dst + c) = make_float4(vals[c], vals[c + 1], vals[c + 2], vals[c + 3]);
+        *reinterpret_cast<float4*>(dst + c) =
+            make_float4(acc[c][r] * inv, acc[c + 1][r] * inv, acc[c + 2][r] * inv, acc[c + 3][r] * inv);
     } else {
       const int64_t prow = row * p.max_partitions + it.part;
       float* dst = p.ws_acc + prow * D + DV * col;
