@@ -33,10 +33,17 @@
  *   is the caller's stream order.
  * Element types.  PA_F32 (IEEE binary32) or PA_BF16 (bfloat16, the upper
  *   16 bits of a binary32).  K, V, new K/V and Q share one element type.
- * Layouts (row-major, contiguous):
- *   k_cache, v_cache   [num_blocks][num_kv_heads][block_size][head_dim]
- *                      -- one (block, KV head) chunk is block_size*head_dim
- *                      contiguous elements
+ * Layouts (row-major, contiguous).  x = 16 / element size (8 for bf16,
+ *   4 for f32): a "granule" is 16 bytes.
+ *   v_cache            [num_blocks][num_kv_heads][block_size][head_dim]
+ *                      -- element d of the token at offset o of a block is
+ *                      v_cache[blk][h][o][d]
+ *   k_cache            [num_blocks][num_kv_heads][head_dim/x][block_size][x]
+ *                      -- element d of the token at offset o of a block is
+ *                      k_cache[blk][h][d/x][o][d%x] (granules token-minor,
+ *                      so the matrix-core operand of 16 keys x 16 bytes is one
+ *                      contiguous run).  In both pools one (block, KV head)
+ *                      chunk is block_size*head_dim contiguous elements.
  *   block_tables       int32 [num_seqs][max_blocks_per_seq]; entry b is the
  *                      physical block of logical block b; entries past the
  *                      last used block are never read (may hold -1)
@@ -113,9 +120,10 @@ pa_status pa_compute_slots(int64_t* slots, const int32_t* block_tables,
  *
  * [gyaansetu] "Apa itu KV Cache?": only the new token's K and V are computed;
  * they are stored so later steps read them back.  For each token j with
- * 0 <= slot_mapping[j] < num_blocks*block_size, and each KV head h:
- *     k_cache[slot / block_size][h][slot % block_size][:] = k_new[j][h][:]
- *     v_cache[...same...]                                 = v_new[j][h][:]
+ * 0 <= slot_mapping[j] < num_blocks*block_size, each KV head h and dim d,
+ * with b = slot / block_size and o = slot % block_size:
+ *     k_cache[b][h][d/x][o][d%x] = k_new[j][h][d]
+ *     v_cache[b][h][o][d]        = v_new[j][h][d]
  * A bit copy (exact).  Negative slots and slots beyond the pool are skipped.
  * Two tokens with the same slot race (caller error).  new_token_stride is
  * the distance in elements between consecutive tokens of k_new and v_new;
@@ -164,16 +172,24 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
  * exact float32 values of the stored elements.
  *
  * max_context_len is a host-side upper bound of every context_lens[i]; it
- * sizes the grid and the workspace (a larger bound is correct, just slower).
- * partition_size splits each context into partitions of that many tokens
- * that are processed independently and merged with an exact log-sum-exp
- * rescale; 0 lets the library choose (pa_decode_partition_size).  A nonzero
- * value must be a multiple of 16 and of block_size.  The workspace (float32
- * partial maxima, sums and outputs) must hold pa_decode_workspace_size()
- * bytes for the same arguments; it may be NULL when that size is 0.
+ * sizes the fixed-partition grid and workspace (a larger bound is correct,
+ * just slower).
+ *
+ * Work decomposition.  With partition_size == 0, bf16 K/V, flags == 0 and
+ * num_seqs <= 8192 the library splits the (sequence, KV head, 16-token tile)
+ * work evenly over one wave per resident wave slot of the device
+ * ("stream-K"); a context shared by two waves is merged from float32
+ * partials with an exact log-sum-exp rescale.  Otherwise each context is cut
+ * into partitions of partition_size tokens (0: the library's choice,
+ * pa_decode_partition_size) processed independently and merged the same way;
+ * a nonzero partition_size must be a multiple of 16 and of block_size and at
+ * most 64 blocks.  The workspace (float32 partials and the decomposition)
+ * must hold pa_decode_workspace_size() bytes for the same arguments, be
+ * 256-byte aligned, and may be NULL when that size is 0.  Calls that share a
+ * workspace must not overlap.
  * flags: 0, or PA_DECODE_VECTOR_ONLY to run the plain vector-ALU kernel
- * instead of the matrix-core kernel (both give results within the same
- * tolerance; the flag exists for cross-checking).
+ * (fixed partitions) instead of the matrix-core kernel; both give results
+ * within the same tolerance, the flag exists for cross-checking.
  * The result is deterministic: it depends on the logical contents and the
  * partitioning only, never on physical block ids or on timing.
  * ------------------------------------------------------------------------- */
@@ -186,7 +202,8 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim,
                                 int32_t block_size, int32_t max_context_len,
-                                int32_t partition_size);
+                                int32_t partition_size, pa_dtype dtype,
+                                uint32_t flags);
 
 pa_status pa_decode_attention(float* out, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_tables,

@@ -24,5 +24,6 @@ from .paged_attention import (  # noqa: F401
     write_kv,
     copy_blocks,
     decode_attention,
+    pool_dims,
     ORACLE_DTYPES,
 )

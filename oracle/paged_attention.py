@@ -30,8 +30,13 @@ Sources (the four pages on PagedAttention; cited by page title and section):
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
 
-* Pool layout: separate K and V pools, each ``[num_blocks][num_kv_heads]
-  [block_size][head_dim]``, row-major.
+* Pool layout: separate K and V pools.  V is ``[num_blocks][num_kv_heads]
+  [block_size][head_dim]`` (one row per token).  K keeps each token's row as
+  16-byte granules of ``x = 16 / element_bytes`` elements, token-minor:
+  ``[num_blocks][num_kv_heads][head_dim / x][block_size][x]``; element ``d`` of
+  token ``o`` of a block is ``K[blk][h][d // x][o][d % x]``.  (The pages fix
+  no in-block layout; this one makes the matrix-core operand loads of the GPU
+  kernel contiguous.)
 * Offset inside a block: token ``p`` sits at offset ``p mod block_size`` of
   logical block ``p // block_size`` (tokens in logical order inside a block,
   as in a page table).
@@ -72,6 +77,23 @@ def to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == F32:
         return np.ascontiguousarray(bits).view(np.float32).astype(np.float64)
     raise ContractError(f"unknown dtype {dtype!r}")
+
+
+def pool_dims(k_pool: np.ndarray, v_pool: np.ndarray):
+    """(num_blocks, num_kv_heads, block_size, head_dim, x) of a K/V pool pair."""
+    if k_pool.ndim != 5 or v_pool.ndim != 4:
+        raise ContractError("K pool must be [NB][Hkv][D/x][bs][x], V pool [NB][Hkv][bs][D]")
+    nb, hkv, dx, bs, x = k_pool.shape
+    if v_pool.shape != (nb, hkv, bs, dx * x):
+        raise ContractError("K and V pools disagree")
+    return nb, hkv, bs, dx * x, x
+
+
+def _k_rows(k_pool: np.ndarray, blocks, heads, offsets) -> np.ndarray:
+    """K rows ``[n][D]`` of tokens (blocks[i], heads, offsets[i]) from the
+    granule layout (a pure re-indexing)."""
+    g = k_pool[blocks, heads, :, offsets, :]          # [n][D/x][x]
+    return g.reshape(g.shape[0], -1)
 
 
 # ---------------------------------------------------------------------------
@@ -139,11 +161,10 @@ def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
     and kept for later steps.  Pools are ``[NB][Hkv][bs][D]``; ``k_new`` and
     ``v_new`` are ``[T][Hkv][D]``.  The copy is of bits, so it is exact for any
     element type.  Slot -1 skips the token; a slot outside the pool or two
-    tokens with the same slot raise.
+    tokens with the same slot raise.  K rows are stored as granules (see the
+    module notes on the layout).
     """
-    num_blocks, num_kv_heads, block_size, head_dim = k_pool.shape
-    if v_pool.shape != k_pool.shape:
-        raise ContractError("K and V pools differ in shape")
+    num_blocks, num_kv_heads, block_size, head_dim, x = pool_dims(k_pool, v_pool)
     slots = np.asarray(slots, dtype=np.int64)
     if k_new.shape != (slots.shape[0], num_kv_heads, head_dim) or v_new.shape != k_new.shape:
         raise ContractError("new K/V must be [T][Hkv][D] matching the slots")
@@ -160,7 +181,7 @@ def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
         if s < 0:
             continue
         b, o = divmod(int(s), block_size)
-        k_out[b, :, o, :] = k_new[j]
+        k_out[b, :, :, o, :] = k_new[j].reshape(num_kv_heads, head_dim // x, x)
         v_out[b, :, o, :] = v_new[j]
     return k_out, v_out
 
@@ -180,7 +201,7 @@ def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs: np.ndarray):
     order of the copies): these raise.
     """
     pairs = np.asarray(pairs).reshape(-1, 2)
-    num_blocks = k_pool.shape[0]
+    num_blocks = pool_dims(k_pool, v_pool)[0]
     if pairs.size and (pairs.min() < 0 or pairs.max() >= num_blocks):
         raise ContractError("pair names a block outside the pool")
     src, dst = pairs[:, 0], pairs[:, 1]
@@ -218,7 +239,7 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         s_t   = scale * <q_h, K_t>          t = 0 .. ctx-1
         out_h = sum_t softmax(s)_t * V_t
 
-    q is ``[S][Hq][D]``; pools ``[NB][Hkv][bs][D]``; the table ``[S][MB]``
+    q is ``[S][Hq][D]``; pools as in the module notes; the table ``[S][MB]``
     (entries past the last used block are never read).  Returns
     ``[S][Hq][D]`` float64; a sequence with ``ctx == 0`` gets zeros.
 
@@ -227,9 +248,9 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     computed are NaN.
     """
     num_seqs, num_q_heads, head_dim = q.shape
-    num_blocks, num_kv_heads, block_size, head_dim_kv = k_pool.shape
-    if head_dim_kv != head_dim or v_pool.shape != k_pool.shape:
-        raise ContractError("q, K and V disagree in head_dim or pool shape")
+    num_blocks, num_kv_heads, block_size, head_dim_kv, _ = pool_dims(k_pool, v_pool)
+    if head_dim_kv != head_dim:
+        raise ContractError("q, K and V disagree in head_dim")
     if num_q_heads % num_kv_heads:
         raise ContractError("num_q_heads must be a multiple of num_kv_heads")
     group = num_q_heads // num_kv_heads
@@ -257,7 +278,7 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
             raise ContractError(f"sequence {i}: table entry is not a pool block")
         for h in head_list:
             g = _kv_head(h, group)
-            k_t = to_f64(k_pool[phys, g, off, :], dtype)        # [n][D]
+            k_t = to_f64(_k_rows(k_pool, phys, g, off), dtype)  # [n][D]
             v_t = to_f64(v_pool[phys, g, off, :], dtype)        # [n][D]
             s = scale64 * (k_t @ q64[i, h])                     # [n]
             w = np.exp(s - s.max())

@@ -4,6 +4,9 @@ Argument marshalling only: every step runs in the HIP kernels of
 ``libpa.so`` behind the C ABI declared in ``include/pa.h``.  There is no CPU
 fallback -- if the library is missing or fails to load, every call raises.
 
+Pools: K is [NB][Hkv][D/x][bs][x] with x = 16 / element size (16-byte
+granules, token-minor), V is [NB][Hkv][bs][D] (see include/pa.h).
+
 Tensors are torch tensors on the current HIP device; element types are
 ``torch.bfloat16`` or ``torch.float32`` for K/V/Q, ``torch.int32`` for block
 tables, context lengths, positions and block mappings, ``torch.int64`` for
@@ -36,7 +39,8 @@ SIGNATURES = {
                                    ctypes.c_int, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
     "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32]),
-    "pa_decode_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                    ctypes.c_int, ctypes.c_uint32]),
     "pa_decode_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                            _I32, _I32, _I32, ctypes.c_float, _I32, _P,
                                            ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32, _P]),
@@ -96,6 +100,21 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _pools(k_cache, v_cache):
+    """(NB, Hkv, bs, D) from the K [NB][Hkv][D/x][bs][x] and V [NB][Hkv][bs][D]
+    pools; checks that they agree and that x is the 16-byte granule."""
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("K pool must be [NB][Hkv][D/x][bs][x] and V pool [NB][Hkv][bs][D]")
+    nb, hkv, dx, bs, x = k_cache.shape
+    if x * k_cache.element_size() != 16:
+        raise ValueError("K pool granule must be 16 bytes")
+    if tuple(v_cache.shape) != (nb, hkv, bs, dx * x):
+        raise ValueError("K and V pools disagree")
+    _need(k_cache, k_cache.dtype, "k_cache")
+    _need(v_cache, k_cache.dtype, "v_cache")
+    return nb, hkv, bs, dx * x
+
+
 def _need(t, dtype, name):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -130,13 +149,9 @@ def compute_slots(block_tables, positions, block_size, num_blocks, seq_ids=None,
 
 
 def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
-    """Store k_new/v_new [T][Hkv][D] in the pools [NB][Hkv][bs][D] at their slots."""
+    """Store k_new/v_new [T][Hkv][D] in the pools at their slots."""
     import torch
-    nb, hkv, bs, d = k_cache.shape
-    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
-        _need(t, k_cache.dtype, name)
-    if v_cache.shape != k_cache.shape:
-        raise ValueError("K and V pools differ in shape")
+    nb, hkv, bs, d = _pools(k_cache, v_cache)
     _need(slot_mapping, torch.int64, "slot_mapping")
     if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
         raise TypeError("new K/V must have the pool's element type")
@@ -153,9 +168,7 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
 def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
     """For each (src, dst) row of block_mapping [n][2]: block dst := block src."""
     import torch
-    nb, hkv, bs, d = k_cache.shape
-    _need(k_cache, k_cache.dtype, "k_cache")
-    _need(v_cache, k_cache.dtype, "v_cache")
+    nb, hkv, bs, d = _pools(k_cache, v_cache)
     _need(block_mapping, torch.int32, "block_mapping")
     n = block_mapping.numel() // 2
     _check("pa_copy_blocks", lib().pa_copy_blocks(
@@ -169,9 +182,14 @@ def decode_partition_size(num_seqs, num_kv_heads, block_size, max_context_len, p
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                          max_context_len, partition_size=0):
+                          max_context_len, partition_size=0, dtype=None, vector_only=False):
+    """Workspace bytes for decode_attention with the same arguments; dtype is
+    a torch dtype (default bfloat16)."""
+    import torch
+    code = PA_F32 if dtype == torch.float32 else PA_BF16
     return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                              block_size, max_context_len, partition_size))
+                                              block_size, max_context_len, partition_size, code,
+                                              PA_DECODE_VECTOR_ONLY if vector_only else 0))
 
 
 def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
@@ -180,16 +198,15 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max
     uint8 device tensor) is allocated here when not given."""
     import torch
     s, hq, d = q.shape
-    nb, hkv, bs, d2 = k_cache.shape
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
     if d2 != d:
         raise ValueError("q and the pools disagree in head_dim")
     _need(q, k_cache.dtype, "q")
-    _need(k_cache, k_cache.dtype, "k_cache")
-    _need(v_cache, k_cache.dtype, "v_cache")
     _need(block_tables, torch.int32, "block_tables")
     _need(context_lens, torch.int32, "context_lens")
     mb = block_tables.shape[1]
-    need = decode_workspace_size(s, hq, hkv, d, bs, max_context_len, partition_size)
+    need = decode_workspace_size(s, hq, hkv, d, bs, max_context_len, partition_size,
+                                 k_cache.dtype, vector_only)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:

@@ -2,6 +2,7 @@
 // and error mapping.  Validation touches scalars and pointer values only and
 // runs before any HIP call, so a rejected call has no effect.
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -40,6 +41,37 @@ int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t bs, int
   };
   while (part / 2 >= floor_part && (part / 2) % unit == 0 && items(part) < kTargetItems) part /= 2;
   return part;
+}
+
+// Stream-K worker count for the current device: one wave per resident wave
+// slot, capped by the workspace slots.  Cached per (device, head_dim); the
+// only state the library keeps.
+int streamk_workers(int head_dim, int* out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  const int k = head_dim == 128 ? 1 : 0;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev][k].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return 0;
+    }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  const int per_cu = pa::streamk_workers_per_cu(head_dim);
+  if (per_cu <= 0) return -1;
+  int64_t w = (int64_t)cus * per_cu;
+  if (w > pa::kStreamKMaxWorkers) w = pa::kStreamKMaxWorkers;
+  w -= w % 4;  // whole workgroups of four waves
+  if (w < 4) w = 4;
+  if (dev < kMaxDevices) cache[dev][k].store((int)w, std::memory_order_relaxed);
+  *out = (int)w;
+  return 0;
 }
 
 }  // namespace
@@ -120,13 +152,18 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
-                                int32_t partition_size) {
-  if (num_q_heads < 1 || !supported_head_dim(head_dim)) return 0;
+                                int32_t partition_size, pa_dtype dtype, uint32_t flags) {
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads ||
+      !supported_head_dim(head_dim) || !valid_dtype(dtype) || num_seqs <= 0)
+    return 0;  // invalid arguments, or no sequence: nothing to hold
+  const bool vector_only = (flags & PA_DECODE_VECTOR_ONLY) != 0;
+  if (pa::decode_path(num_seqs, dtype, partition_size, vector_only) == pa::DecodePath::kStreamK)
+    return pa::decode_workspace_streamk(num_seqs, num_q_heads / num_kv_heads, head_dim).total;
   const int32_t part = pa_decode_partition_size(num_seqs, num_kv_heads, block_size,
                                                 max_context_len, partition_size);
   if (part <= 0) return 0;
   const int64_t P = max_context_len > 0 ? (max_context_len + (int64_t)part - 1) / part : 1;
-  return pa::decode_workspace(num_seqs, num_q_heads, head_dim, (int)P).total;
+  return pa::decode_workspace_partition(num_seqs, num_q_heads, head_dim, (int)P).total;
 }
 
 pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, const void* v_cache,
@@ -147,16 +184,21 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, co
   if (partition_size != 0 && !valid_partition(partition_size, block_size)) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
   const int32_t max_tokens = max_blocks_per_seq * block_size;
-  // Same partition and partition count as pa_decode_workspace_size.
+  const bool vector_only = (flags & PA_DECODE_VECTOR_ONLY) != 0;
+  const pa::DecodePath path = pa::decode_path(num_seqs, dtype, partition_size, vector_only);
+  // Same partition, partition count and workspace as pa_decode_workspace_size.
   const int32_t part = partition_size ? partition_size
                                       : choose_partition(num_seqs, num_kv_heads, block_size,
                                                          max_context_len);
   const int64_t P = max_context_len > 0 ? (max_context_len + (int64_t)part - 1) / part : 1;
   if ((int64_t)num_seqs * num_kv_heads * P / 4 >= INT32_MAX) return PA_ERR_SHAPE;
-  const pa::DecodeWorkspace ws = pa::decode_workspace(num_seqs, num_q_heads, head_dim, (int)P);
+  if (num_seqs == 0) return PA_OK;
+  const pa::DecodeWorkspace ws =
+      path == pa::DecodePath::kStreamK
+          ? pa::decode_workspace_streamk(num_seqs, num_q_heads / num_kv_heads, head_dim)
+          : pa::decode_workspace_partition(num_seqs, num_q_heads, head_dim, (int)P);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PA_ERR_WORKSPACE;
   if (ws.total > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PA_ERR_WORKSPACE;
-  if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_UNSUPPORTED;
@@ -169,21 +211,35 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, co
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   char* wsb = static_cast<char*>(workspace);
-  p.ws_m = ws.total ? reinterpret_cast<float*>(wsb + ws.m_off) : nullptr;
-  p.ws_l = ws.total ? reinterpret_cast<float*>(wsb + ws.l_off) : nullptr;
-  p.ws_acc = ws.total ? reinterpret_cast<float*>(wsb + ws.acc_off) : nullptr;
+  if (ws.total) {
+    p.ws_m = reinterpret_cast<float*>(wsb + ws.m_off);
+    p.ws_l = reinterpret_cast<float*>(wsb + ws.l_off);
+    p.ws_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
+    if (path == pa::DecodePath::kStreamK) {
+      p.ws_prefix = reinterpret_cast<int32_t*>(wsb + ws.prefix_off);
+      p.ws_header = reinterpret_cast<int64_t*>(wsb + ws.header_off);
+    }
+  }
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.num_blocks = num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
-  p.partition = part;
-  p.max_partitions = (int)P;
-  p.max_tokens = (int)((int64_t)P * part < max_tokens ? (int64_t)P * part : max_tokens);
   p.scale_log2 = scale * 1.4426950408889634f;
-  return from_hip(pa::launch_decode(p, head_dim, block_size, dtype,
-                                    (flags & PA_DECODE_VECTOR_ONLY) != 0,
+  if (path == pa::DecodePath::kStreamK) {
+    int workers = 0;
+    if (streamk_workers(head_dim, &workers) != 0) return PA_ERR_HIP;
+    p.max_workers = workers;
+    p.partition = 16;
+    p.max_partitions = 1;
+    p.max_tokens = max_tokens;
+  } else {
+    p.partition = part;
+    p.max_partitions = (int)P;
+    p.max_tokens = (int)((int64_t)P * part < max_tokens ? (int64_t)P * part : max_tokens);
+  }
+  return from_hip(pa::launch_decode(p, head_dim, block_size, dtype, vector_only, path,
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -6,9 +6,10 @@
 //    penempatan fisik": logical block b of a sequence lives in physical block
 //    table[b]; a token keeps its logical order inside its block.
 //  * The write stores only the new tokens' K/V ([gyaansetu] "Apa itu KV
-//    Cache?").  Pool layout [NB][Hkv][bs][D]: one token of one KV head is a
-//    D-element row, so a token scatters Hkv rows of D*e bytes (256 B for bf16,
-//    D=128), each written with full 16-byte stores.
+//    Cache?").  V pool [NB][Hkv][bs][D]: one token of one KV head is a
+//    D-element row (256 B for bf16, D=128).  K pool [NB][Hkv][D/x][bs][x]: the
+//    same row split into 16-byte granules, granule w stored at [w][offset].
+//    Every store is a full 16-byte granule.
 //  * The block copy gives a diverging branch its own copy of a shared block
 //    ([nalar] "Sharing blok dapat menghindari duplikasi state KV"); a block is
 //    Hkv*bs*D*e contiguous bytes in each pool, streamed with 16-byte loads.
@@ -38,8 +39,8 @@ __global__ __launch_bounds__(256) void compute_slots_kernel(
   slots[j] = slot;
 }
 
-// One wave per token; each lane moves 16-byte chunks of the token's
-// [Hkv][D] row into the Hkv scattered rows of its slot.
+// One wave per token; each lane moves 16-byte granules of the token's
+// [Hkv][D] row to their places in the two pools.
 constexpr int kWriteWaves = 4;
 
 __global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_kernel(
@@ -61,11 +62,12 @@ __global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_kernel(
   for (int c = lane; c < nchunks; c += kWave) {
     const int h = c / head_chunks;
     const int w = c - h * head_chunks;
-    const int64_t dst = (((blk * num_kv_heads + h) * block_size + off) * head_chunks + w) * 16;
+    const int64_t kdst = (((blk * num_kv_heads + h) * head_chunks + w) * block_size + off) * 16;
+    const int64_t vdst = (((blk * num_kv_heads + h) * block_size + off) * head_chunks + w) * 16;
     const uint4 a = *reinterpret_cast<const uint4*>(ksrc + (int64_t)c * 16);
     const uint4 b = *reinterpret_cast<const uint4*>(vsrc + (int64_t)c * 16);
-    *reinterpret_cast<uint4*>(k_cache + dst) = a;
-    *reinterpret_cast<uint4*>(v_cache + dst) = b;
+    *reinterpret_cast<uint4*>(k_cache + kdst) = a;
+    *reinterpret_cast<uint4*>(v_cache + vdst) = b;
   }
 }
 

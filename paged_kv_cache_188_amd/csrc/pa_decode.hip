@@ -7,34 +7,50 @@
 // logical blocks in order and translates each through the block table before
 // loading the block's K and V rows.
 //
-// Work decomposition (not on the pages; a gfx950 design):
-//   one wave = one work item (sequence, KV head, context partition).  All
-//   G = Hq/Hkv query heads of the KV head are served by that wave, so every
-//   K/V row is read from HBM once per KV head.  A context longer than one
-//   partition is split over several waves whose float32 partial results
-//   (running max, running sum, unnormalised output) are merged exactly by
-//   decode_reduce_kernel (log-sum-exp rescale, fixed order).
+// Work decomposition (not on the pages; a gfx950 design).  A "segment" is one
+// (sequence, KV head): all G = Hq/Hkv query heads of the KV head are served by
+// the same wave, so every K/V row is read from HBM once per KV head.  Segments
+// are cut into 16-token tiles.
+//   * stream-K path (bf16, the default): persistent waves, one per resident
+//     wave slot.  The tiles of all segments, in (sequence, KV head, tile)
+//     order, are split into equal contiguous ranges, one per wave, so every
+//     wave streams the same number of bytes whatever the length mix.  A wave
+//     writes the final output of every segment it covers whole and a float32
+//     partial (running max, running sum, unnormalised output) for at most two
+//     segments it shares with its neighbours; decode_streamk_merge_kernel
+//     combines those (log-sum-exp rescale, fixed order).
+//   * fixed-partition path (float32 K/V, an explicit partition size, or very
+//     large batches): one wave per (segment, partition) work item, partials
+//     merged by decode_reduce_kernel.
 //
-// Matrix-core kernel (bf16 K/V, the serving configurations):
-//   a tile is 16 consecutive logical tokens.
-//   QK^T : v_mfma_f32_16x16x32_bf16, A = 16 key rows x 32 dims, B = 32 dims x
-//          16 query heads (heads >= G are zero).  bf16 x bf16 products are
-//          exact in float32 and accumulate in float32.
-//          Lane (grp = lane/16, col = lane%16) loads key row `col`, dims
-//          32*s + 8*grp .. +7 of each k-step s (16-byte loads).
-//          Result: lane holds scores of head `col` for tokens 4*grp + i.
+// Matrix-core tile loop (bf16 K/V):
+//   a tile is 16 consecutive logical tokens.  Loads are laid out so that
+//   every group of four consecutive lanes reads 64 contiguous bytes and every
+//   group of sixteen reads 256 contiguous bytes.  (Measured on MI355X: a random
+//   4 KiB chunk gather reaches ~6.0 TB/s with that pattern but only ~4.7 TB/s
+//   when the four lanes of a group read four different 256-byte rows, which is
+//   what a token-major K row would need for the matrix-core operand.)  K/V are
+//   read once, so the loads are non-temporal.
+//   QK^T : v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims, B = 32 dims x 16
+//          query heads (heads >= G are zero).  bf16 x bf16 products are exact
+//          in float32 and accumulate in float32.  The K pool stores 16-byte
+//          granules token-minor, so lane (grp = lane/16, col = lane%16) reads
+//          granule 4*s + grp of key `col`.  Result: lane holds the scores of
+//          head `col` for tokens 4*grp + i.
 //   softmax: online (running max m, running sum l) per head, base 2 with the
 //          scale folded in; masked tokens get -inf by select, never by
 //          multiplication, so NaN in unused slots cannot leak.
 //   PV   : v_mfma_f32_16x16x4_f32, A = P (16 heads x 4 tokens, full float32),
-//          B = V (4 tokens x 16 dims).  The token order inside the k-step is
-//          free, so lane (grp, col) uses its own score registers (token
-//          4*grp + j in step j) and its own V load: row 4*grp + j, dims
-//          (D/16)*col .. +D/16-1 -- 16 lanes read one V row contiguously.
+//          B = V (4 tokens x 16 dims).  The token order inside a k-step is
+//          free, so step j uses lane (grp, col)'s own score register j (token
+//          4*grp + j) and its own V load: row 4*grp + j, dims (D/16)*col ..
+//          +D/16-1 of the token-major V pool (16 lanes read one V row).
 //          Output: lane holds heads 4*grp + r, dims (D/16)*col + nt.
+//   pipeline: a ring of 4 tiles in registers, 3 in flight while one is
+//          computed.
 //
-// Vector-ALU kernel (float32 K/V, or on request): 16-byte row chunks, LPR
-//   lanes per row, each group of LPR lanes an independent online-softmax
+// Vector-ALU kernel (float32 K/V, or on request): 16-byte granules, LPR
+//   lanes per token, each group of LPR lanes an independent online-softmax
 //   stream over every (64/LPR)-th token; the streams are merged at the end
 //   with a fixed butterfly, so results are deterministic.
 
@@ -47,8 +63,10 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kDecodeWaves = 4;  // independent work items per workgroup
+constexpr int kDecodeWaves = 4;  // independent waves per workgroup
 constexpr int kRing = 4;         // 16-token tiles held in registers per wave (3 in flight)
 constexpr float kLazyMax = 8.f;  // headroom (log2) before the running max must move
 constexpr float kNegInf = -__builtin_inff();
@@ -61,162 +79,175 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-struct Item {
-  int seq, kvh, part, n, nparts, start, end;
-};
+// Streaming (non-temporal) loads of K/V data that is read exactly once.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  return __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)));
+}
 
-// Decode the flat work-item index; returns false for waves with no work.
-__device__ __forceinline__ bool decode_item(const DecodeParams& p, int64_t item, Item& it) {
-  const int P = p.max_partitions;
-  const int64_t rest = item / P;
-  if (rest >= (int64_t)p.num_seqs * p.num_kv_heads) return false;
-  it.part = (int)(item - rest * P);
-  it.kvh = (int)(rest % p.num_kv_heads);
-  it.seq = (int)(rest / p.num_kv_heads);
-  int n = p.context_lens[it.seq];
-  n = min(max(n, 0), p.max_tokens);
-  it.n = n;
-  it.nparts = (n + p.partition - 1) / p.partition;
-  if (it.part >= max(it.nparts, 1)) return false;
-  it.start = it.part * p.partition;
-  it.end = min(it.start + p.partition, n);
-  return true;
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+__device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int seq) {
+  return min(max(p.context_lens[seq], 0), p.max_tokens);
 }
 
 // ---------------------------------------------------------------------------
-// matrix-core kernel (bf16)
+// matrix-core building blocks (bf16)
 // ---------------------------------------------------------------------------
 
+template <int D>
+struct MfmaState {
+  f32x4_t acc[D / 16];
+  float m_run;  // reference point of the exponentials of head `col` (log2)
+  float l_run;  // per-lane partial sum of weights of head `col`
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run = kNegInf;
+    l_run = 0.f;
+  }
+};
+
+// Query heads hq0 .. hq0+G-1 of sequence `seq` as the B operand of QK^T
+// (zero rows for col >= G).
+template <int D>
+__device__ __forceinline__ void mfma_load_q(const DecodeParams& p, int seq, int hq0, int lane,
+                                            bf16x8_t (&qv)[D / 32]) {
+  const int grp = lane >> 4, col = lane & 15;
+  const bool valid = col < p.group;
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                         ((int64_t)seq * p.num_q_heads + hq0 + (valid ? col : 0)) * D;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (valid) raw = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * grp);
+    qv[s] = as_bf16x8(raw);
+  }
+}
+
+// Tiles [tile_begin, tile_end) of segment (seq, kvh) whose context is n
+// tokens, accumulated into st.  The tiles may touch at most 64 blocks (one
+// block id per lane).
+//
+// The running max is moved only when a score exceeds it by more than
+// kLazyMax, so every weight 2^(x - m_run) stays <= 2^kLazyMax and the common
+// path needs no cross-lane traffic; results are exact either way (partials
+// carry m_run as their reference point).
 template <int D, int BS>
-__global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(const DecodeParams p) {
-  static_assert(D == 64 || D == 128, "head_dim");
+__device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int kvh, int n,
+                                           int tile_begin, int tile_end,
+                                           const bf16x8_t (&qv)[D / 32], MfmaState<D>& st,
+                                           int lane) {
   constexpr int KSTEPS = D / 32;  // QK k-steps
   constexpr int DV = D / 16;      // V dims per lane per row == PV n-tiles
   using VRow = typename std::conditional<DV == 8, uint4, uint2>::type;
   struct Tile {
-    uint4 k[KSTEPS];  // key row `col`, dims 32*s + 8*grp .. +7
-    VRow v[4];        // value rows 4*grp + j, dims DV*col .. +DV-1
+    uint4 k[KSTEPS];  // key `col`, granule 4*s + grp (dims 32*s + 8*grp .. +7)
+    VRow v[4];        // value row 4*grp + j, dims DV*col .. +DV-1
   };
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
   const int grp = lane >> 4;
   const int col = lane & 15;
-  Item it;
-  if (!decode_item(p, (int64_t)blockIdx.x * kDecodeWaves + wave, it)) return;
-  const int G = p.group;
-  const int hq0 = it.kvh * G;
+  const int start = 16 * tile_begin;
+  const int end = min(16 * tile_end, n);
+  const int ntiles = tile_end - tile_begin;
+  if (ntiles <= 0) return;
 
-  // Query heads as the B operand of QK^T (zero rows for col >= G).
-  bf16x8_t qv[KSTEPS];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           ((int64_t)it.seq * p.num_q_heads + hq0 + (col < G ? col : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (col < G) raw = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * grp);
-      qv[s] = as_bf16x8(raw);
-    }
-  }
-
-  // Physical ids of the partition's blocks, one per lane (partition <= 64 blocks).
-  const int b0 = it.start / BS;
-  const int nblk = (it.end - it.start + BS - 1) / BS;
+  // Physical ids of the blocks the tiles touch, one per lane.
+  const int b0 = start / BS;
+  const int nblk = (end - 1) / BS - b0 + 1;
   int my_id = 0;
   if (lane < nblk) {
-    const int v = p.block_tables[(int64_t)it.seq * p.max_blocks_per_seq + b0 + lane];
+    const int v = p.block_tables[(int64_t)seq * p.max_blocks_per_seq + b0 + lane];
     my_id = (v >= 0 && v < p.num_blocks) ? v : 0;  // a bad entry reads block 0, never faults
   }
 
   const uint16_t* kpool = static_cast<const uint16_t*>(p.k_cache);
   const uint16_t* vpool = static_cast<const uint16_t*>(p.v_cache);
-  const int64_t chunk = (int64_t)BS * D;  // elements of one (block, KV head) chunk
   auto chunk_base = [&](int phys) -> int64_t {
-    return ((int64_t)phys * p.num_kv_heads + it.kvh) * chunk;
+    return ((int64_t)phys * p.num_kv_heads + kvh) * ((int64_t)BS * D);
   };
-  const int ntiles = (it.end - it.start + 15) / 16;
 
-  // Tile t covers tokens start+16t .. +15.  For BS >= 16 they lie in one
-  // block, whose id is wave-uniform (readlane); for BS == 8 a tile spans two
-  // blocks and each lane fetches its row's id with a lane shuffle.  Rows past
-  // the partition's last block reuse its id (they are masked).  The index is
-  // clamped to the last tile, so the ring can be refilled unconditionally:
-  // loads past the end re-read the last tile (from cache) and are never used.
+  // Tile index clamped to the last tile: the ring is refilled
+  // unconditionally, and a refill past the end reads one 16-byte granule per
+  // instruction (all lanes the same address), never used.
   auto load = [&](int t, Tile& b) {
-    const int tb = it.start + 16 * min(t, ntiles - 1);
+    const bool past = t >= ntiles;
+    const int tb = start + 16 * min(t, ntiles - 1);
     if constexpr (BS >= 16) {
       const int phys = __builtin_amdgcn_readlane(my_id, tb / BS - b0);
-      const int64_t cb = chunk_base(phys) + (int64_t)(tb % BS) * D;
-      const uint16_t* kb = kpool + cb + (int64_t)col * D + 8 * grp;
+      const int64_t cb = chunk_base(phys);
+      const int o = tb % BS;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) b.k[s] = *reinterpret_cast<const uint4*>(kb + 32 * s);
+      for (int s = 0; s < KSTEPS; ++s)
+        b.k[s] = load_stream(reinterpret_cast<const uint4*>(
+            kpool + cb + (past ? 0 : ((int64_t)(4 * s + grp) * BS + o + col) * 8)));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b.v[j] = *reinterpret_cast<const VRow*>(vpool + cb + (int64_t)(4 * grp + j) * D + DV * col);
+        b.v[j] = load_stream(reinterpret_cast<const VRow*>(
+            vpool + cb + (past ? 0 : (int64_t)(o + 4 * grp + j) * D + DV * col)));
     } else {
-      auto row_base = [&](int tok) -> int64_t {
+      auto blk_base = [&](int tok) -> int64_t {
         const int lb = min(tok / BS - b0, nblk - 1);
-        return chunk_base(__shfl(my_id, lb)) + (int64_t)(tok % BS) * D;
+        return chunk_base(__shfl(my_id, lb));
       };
-      const uint16_t* kb = kpool + row_base(tb + col) + 8 * grp;
+      const int kt = tb + col;
+      const int64_t kb = blk_base(kt);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) b.k[s] = *reinterpret_cast<const uint4*>(kb + 32 * s);
+      for (int s = 0; s < KSTEPS; ++s)
+        b.k[s] = load_stream(reinterpret_cast<const uint4*>(
+            kpool + kb + (past ? 0 : ((int64_t)(4 * s + grp) * BS + kt % BS) * 8)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b.v[j] = *reinterpret_cast<const VRow*>(vpool + row_base(tb + 4 * grp + j) + DV * col);
+      for (int j = 0; j < 4; ++j) {
+        const int vt = tb + 4 * grp + j;
+        b.v[j] = load_stream(reinterpret_cast<const VRow*>(
+            vpool + blk_base(vt) + (past ? 0 : (int64_t)(vt % BS) * D + DV * col)));
+      }
     }
   };
 
-  f32x4_t acc[DV];
-#pragma unroll
-  for (int nt = 0; nt < DV; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // m_run: reference point of the exponentials of head `col` (log2 domain).
-  // It is moved only when a score exceeds it by more than kLazyMax, so every
-  // weight 2^(x - m_run) stays <= 2^kLazyMax and the common path needs no
-  // cross-lane traffic; results are exact either way (partials carry m_run).
-  float m_run = kNegInf;
-  float l_run = 0.f;
-
   auto compute = [&](int t, Tile& b) {
-    const int tb = it.start + 16 * t;
+    const int tb = start + 16 * t;
     // scores: lane holds head `col`, tokens tb + 4*grp + i
     f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(b.k[s]), qv[s], sc, 0, 0, 0);
-    const bool full = tb + 16 <= it.end;
+    const bool full = tb + 16 <= end;
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = full || (tb + 4 * grp + i < it.end);
+      const bool ok = full || (tb + 4 * grp + i < end);
       x[i] = ok ? sc[i] * p.scale_log2 : kNegInf;
     }
     const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    if (__any(lmax > m_run + kLazyMax)) {
+    if (__any(lmax > st.m_run + kLazyMax)) {
       float mt = fmaxf(lmax, __shfl_xor(lmax, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
-      l_run *= alpha;
+      const float m_new = fmaxf(st.m_run, mt);
+      const float alpha = fast_exp2(st.m_run - m_new);  // 0 on the first tile
+      st.l_run *= alpha;
       // rows of acc are heads 4*grp + r; their factor lives in lane 4*grp + r
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = __shfl(alpha, 4 * grp + r);
 #pragma unroll
-        for (int nt = 0; nt < DV; ++nt) acc[nt][r] *= a;
+        for (int nt = 0; nt < DV; ++nt) st.acc[nt][r] *= a;
       }
-      m_run = m_new;
+      st.m_run = m_new;
     }
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - m_run);
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - st.m_run);
+    st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     if (!full) {  // zero V rows past the end (they may hold anything, NaN included)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (tb + 4 * grp + j >= it.end) b.v[j] = VRow{};
+        if (tb + 4 * grp + j >= end) b.v[j] = VRow{};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -224,79 +255,303 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(co
 #pragma unroll
       for (int nt = 0; nt < DV; ++nt) {
         const float v = (nt & 1) ? bf16_hi(w[nt >> 1]) : bf16_lo(w[nt >> 1]);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[j], v, acc[nt], 0, 0, 0);
+        st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[j], v, st.acc[nt], 0, 0, 0);
       }
     }
   };
 
-  if (ntiles > 0) {
-    // The first pass only fills the ring, so every path into a compute has
-    // issued the ring's loads in the same order (the compiler can then wait
-    // for the oldest tile alone).
-    Tile ring[kRing];
-    for (int t0 = -kRing; t0 < ntiles; t0 += kRing) {
+  // The first pass only fills the ring, so every path into a compute has
+  // issued the ring's loads in the same order (the compiler can then wait for
+  // the oldest tile alone).
+  Tile ring[kRing];
+  for (int t0 = -kRing; t0 < ntiles; t0 += kRing) {
 #pragma unroll
-      for (int i = 0; i < kRing; ++i) {
-        const int t = t0 + i;
-        if (t >= 0 && t < ntiles) compute(t, ring[i]);
-        load(t + kRing, ring[i]);
-      }
+    for (int i = 0; i < kRing; ++i) {
+      const int t = t0 + i;
+      if (t >= 0 && t < ntiles) compute(t, ring[i]);
+      load(t + kRing, ring[i]);
     }
   }
+}
 
+// Tiles [tile_begin, tile_end) of a segment in calls of at most 64 blocks.
+template <int D, int BS>
+__device__ __forceinline__ void mfma_segment(const DecodeParams& p, int seq, int kvh, int n,
+                                             int tile_begin, int tile_end,
+                                             const bf16x8_t (&qv)[D / 32], MfmaState<D>& st,
+                                             int lane) {
+  // at most 64 blocks: a range of 63*BS tokens starting anywhere in a block
+  // (tiles start on 16-token boundaries; for BS == 8 they start on blocks)
+  constexpr int kMaxTiles = BS >= 16 ? (63 * BS) / 16 : 32;
+  for (int t = tile_begin; t < tile_end; t += kMaxTiles)
+    mfma_tiles<D, BS>(p, seq, kvh, n, t, min(t + kMaxTiles, tile_end), qv, st, lane);
+}
+
+// Write the G heads of a finished state: normalised into `out_row0` (head h
+// at out_row0 + h*D), or as a partial: acc at acc_row0 + h*acc_stride, m and
+// l at m0/l0 + h*ml_stride.
+template <int D>
+__device__ __forceinline__ void mfma_finish(MfmaState<D>& st, int G, int lane, float* out_row0,
+                                            float* acc_row0, float* m0, float* l0,
+                                            int64_t acc_stride, int64_t ml_stride) {
+  constexpr int DV = D / 16;
+  const int grp = lane >> 4, col = lane & 15;
   // total running sum per head (lanes of one column hold the same head)
+  float l_run = st.l_run;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-
-  const bool single = it.nparts <= 1;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * grp + r;
     const float l_h = __shfl(l_run, h);
-    const float m_h = __shfl(m_run, h);
+    const float m_h = __shfl(st.m_run, h);
     if (h >= G) continue;
-    const int64_t row = (int64_t)it.seq * p.num_q_heads + hq0 + h;
-    if (single) {
+    if (out_row0) {
       const float inv = l_h > 0.f ? 1.0f / l_h : 0.f;
-      float* dst = p.out + row * D + DV * col;
+      float* dst = out_row0 + (int64_t)h * D + DV * col;
 #pragma unroll
       for (int c = 0; c < DV; c += 4)
-        *reinterpret_cast<float4*>(dst + c) =
-            make_float4(acc[c][r] * inv, acc[c + 1][r] * inv, acc[c + 2][r] * inv, acc[c + 3][r] * inv);
+        *reinterpret_cast<float4*>(dst + c) = make_float4(
+            st.acc[c][r] * inv, st.acc[c + 1][r] * inv, st.acc[c + 2][r] * inv, st.acc[c + 3][r] * inv);
     } else {
-      const int64_t prow = row * p.max_partitions + it.part;
-      float* dst = p.ws_acc + prow * D + DV * col;
+      float* dst = acc_row0 + (int64_t)h * acc_stride + DV * col;
 #pragma unroll
       for (int c = 0; c < DV; c += 4)
         *reinterpret_cast<float4*>(dst + c) =
-            make_float4(acc[c][r], acc[c + 1][r], acc[c + 2][r], acc[c + 3][r]);
+            make_float4(st.acc[c][r], st.acc[c + 1][r], st.acc[c + 2][r], st.acc[c + 3][r]);
       if (col == 0) {
-        p.ws_m[prow] = m_h;
-        p.ws_l[prow] = l_h;
+        m0[(int64_t)h * ml_stride] = m_h;
+        l0[(int64_t)h * ml_stride] = l_h;
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// vector-ALU kernel (f32 or bf16)
+// stream-K matrix-core kernel
 // ---------------------------------------------------------------------------
+
+// Exclusive prefix over sequences of their tile counts, into LDS (S+1
+// entries), computed by the whole workgroup.
+__device__ void tile_prefix(const DecodeParams& p, int* s_prefix) {
+  __shared__ int wave_sums[kDecodeWaves];
+  __shared__ int carry_s;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < p.num_seqs; base += kDecodeWaves * kWave) {
+    const int i = base + tid;
+    int v = 0;
+    if (i < p.num_seqs) v = (clamp_ctx(p, i) + 15) / 16;
+    // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    if (lane == kWave - 1) wave_sums[wave] = v;
+    __syncthreads();
+    int before = carry_s;
+    for (int w = 0; w < wave; ++w) before += wave_sums[w];
+    if (i < p.num_seqs) s_prefix[i + 1] = before + v;
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int w = 0; w < kDecodeWaves; ++w) tot += wave_sums[w];
+      carry_s += tot;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) s_prefix[0] = 0;
+  __syncthreads();
+}
+
+__device__ __forceinline__ int64_t streamk_workers(int64_t total_tiles, int launched) {
+  const int64_t want = (total_tiles + kStreamKMinTiles - 1) / kStreamKMinTiles;
+  return want < launched ? (want > 0 ? want : 1) : launched;
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_kernel(
+    const DecodeParams p) {
+  extern __shared__ int s_prefix[];  // [S+1]
+  tile_prefix(p, s_prefix);
+  const int S = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
+  const int64_t T = (int64_t)Hkv * s_prefix[S];
+  const int64_t W = streamk_workers(T, p.max_workers);
+  if (blockIdx.x == 0) {  // publish the decomposition for the merge kernel
+    for (int i = threadIdx.x; i <= S; i += blockDim.x) p.ws_prefix[i] = s_prefix[i];
+    if (threadIdx.x == 0) {
+      p.ws_header[0] = T;
+      p.ws_header[1] = W;
+    }
+  }
+  const int lane = threadIdx.x % kWave;
+  const int64_t w = (int64_t)blockIdx.x * kDecodeWaves + wave_id();
+  if (T == 0 || w >= W) return;
+  const int64_t g0 = w * T / W;
+  const int64_t g1 = (w + 1) * T / W;
+  const int G = p.group;
+
+  // segment holding tile g0: the last sequence whose first tile is <= g0
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if ((int64_t)Hkv * s_prefix[mid] <= g0) lo = mid; else hi = mid - 1;
+  }
+  int seq = lo;
+  int nt = s_prefix[seq + 1] - s_prefix[seq];
+  int64_t seq0 = (int64_t)Hkv * s_prefix[seq];
+  int kvh = (int)((g0 - seq0) / nt);
+  int tb = (int)((g0 - seq0) - (int64_t)kvh * nt);
+  int64_t g = g0;
+
+  const int64_t slot0 = w * 2;
+  MfmaState<D> st;
+  bf16x8_t qv[D / 32];
+  while (g < g1) {
+    const int64_t seg_start = seq0 + (int64_t)kvh * nt;
+    const int te = (int)min<int64_t>(nt, g1 - seg_start);
+    const int n = clamp_ctx(p, seq);
+    const int hq0 = kvh * G;
+    mfma_load_q<D>(p, seq, hq0, lane, qv);
+    st.reset();
+    mfma_segment<D, BS>(p, seq, kvh, n, tb, te, qv, st, lane);
+    if (tb == 0 && te == nt) {
+      mfma_finish<D>(st, G, lane, p.out + ((int64_t)seq * p.num_q_heads + hq0) * D, nullptr,
+                     nullptr, nullptr, 0, 0);
+    } else {
+      // slot 0: a segment begun by an earlier wave; slot 1: one continued by a later wave
+      const int64_t slot = slot0 + (tb > 0 ? 0 : 1);
+      mfma_finish<D>(st, G, lane, nullptr, p.ws_acc + slot * G * D, p.ws_m + slot * G,
+                     p.ws_l + slot * G, D, 1);
+    }
+    g += te - tb;
+    tb = 0;
+    if (++kvh == Hkv) {
+      kvh = 0;
+      do {
+        ++seq;
+      } while (seq < S && s_prefix[seq + 1] == s_prefix[seq]);
+      if (seq >= S) break;
+      nt = s_prefix[seq + 1] - s_prefix[seq];
+      seq0 = (int64_t)Hkv * s_prefix[seq];
+    }
+  }
+}
+
+// One workgroup per segment (sequence, KV head).  Segments split across
+// waves are merged from their partials: slot 1 of the first wave, slot 0 of
+// the others (in wave order); an empty segment gets zeros.
+template <int D>
+__global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeParams p) {
+  constexpr int C = D / 4;  // float4 chunks per row
+  const int e = blockIdx.x;
+  const int Hkv = p.num_kv_heads;
+  const int seq = e / Hkv, kvh = e % Hkv;
+  const int G = p.group;
+  const int hq0 = kvh * G;
+  const int nt = p.ws_prefix[seq + 1] - p.ws_prefix[seq];
+  float* out = p.out + ((int64_t)seq * p.num_q_heads + hq0) * D;
+  if (nt == 0) {
+    for (int idx = threadIdx.x; idx < G * C; idx += blockDim.x)
+      reinterpret_cast<float4*>(out)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int64_t T = p.ws_header[0];
+  const int64_t W = p.ws_header[1];
+  const int64_t first = (int64_t)Hkv * p.ws_prefix[seq] + (int64_t)kvh * nt;
+  const int64_t w1 = ((first + 1) * W - 1) / T;           // wave owning the first tile
+  const int64_t w2 = ((first + nt) * W - 1) / T;          // wave owning the last tile
+  if (w1 == w2) return;                                    // written whole by one wave
+  for (int idx = threadIdx.x; idx < G * C; idx += blockDim.x) {
+    const int h = idx / C, c = idx % C;
+    float M = kNegInf;
+    for (int64_t w = w1; w <= w2; ++w) {
+      const int64_t slot = 2 * w + (w == w1 ? 1 : 0);
+      M = fmaxf(M, p.ws_m[slot * G + h]);
+    }
+    float L = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t w = w1; w <= w2; ++w) {
+      const int64_t slot = 2 * w + (w == w1 ? 1 : 0);
+      const float wt = fast_exp2(p.ws_m[slot * G + h] - M);
+      L = fmaf(wt, p.ws_l[slot * G + h], L);
+      const float4 v = reinterpret_cast<const float4*>(p.ws_acc + (slot * G + h) * D)[c];
+      a.x = fmaf(wt, v.x, a.x);
+      a.y = fmaf(wt, v.y, a.y);
+      a.z = fmaf(wt, v.z, a.z);
+      a.w = fmaf(wt, v.w, a.w);
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    reinterpret_cast<float4*>(out + (int64_t)h * D)[c] =
+        make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fixed-partition kernels
+// ---------------------------------------------------------------------------
+
+struct Item {
+  int seq, kvh, part, n, nparts, start, end;
+};
+
+// Decode the flat work-item index (part fastest); false for waves with no work.
+__device__ __forceinline__ bool decode_item(const DecodeParams& p, int64_t item, Item& it) {
+  const int P = p.max_partitions;
+  const int64_t rest = item / P;
+  if (rest >= (int64_t)p.num_seqs * p.num_kv_heads) return false;
+  it.part = (int)(item - rest * P);
+  it.kvh = (int)(rest % p.num_kv_heads);
+  it.seq = (int)(rest / p.num_kv_heads);
+  it.n = clamp_ctx(p, it.seq);
+  it.nparts = (it.n + p.partition - 1) / p.partition;
+  if (it.part >= max(it.nparts, 1)) return false;
+  it.start = it.part * p.partition;
+  it.end = min(it.start + p.partition, it.n);
+  return true;
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(const DecodeParams p) {
+  const int lane = threadIdx.x % kWave;
+  Item it;
+  if (!decode_item(p, (int64_t)blockIdx.x * kDecodeWaves + wave_id(), it)) return;
+  const int G = p.group;
+  const int hq0 = it.kvh * G;
+  bf16x8_t qv[D / 32];
+  mfma_load_q<D>(p, it.seq, hq0, lane, qv);
+  MfmaState<D> st;
+  st.reset();
+  // a partition is a whole number of tiles and at most 64 blocks
+  mfma_tiles<D, BS>(p, it.seq, it.kvh, it.n, it.start / 16, (it.end + 15) / 16, qv, st, lane);
+  const int64_t row = (int64_t)it.seq * p.num_q_heads + hq0;
+  if (it.nparts <= 1) {
+    mfma_finish<D>(st, G, lane, p.out + row * D, nullptr, nullptr, nullptr, 0, 0);
+  } else {
+    const int64_t prow = row * p.max_partitions + it.part;
+    mfma_finish<D>(st, G, lane, nullptr, p.ws_acc + prow * D, p.ws_m + prow, p.ws_l + prow,
+                   (int64_t)p.max_partitions * D, p.max_partitions);
+  }
+}
 
 template <typename T, int D, int GMAX>
 __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_valu_kernel(const DecodeParams p,
                                                                            int block_size) {
   constexpr int E = sizeof(T);
-  constexpr int VEC = 16 / E;    // elements per lane per row chunk
-  constexpr int LPR = D / VEC;   // lanes per row
+  constexpr int VEC = 16 / E;    // elements per lane per 16-byte granule
+  constexpr int LPR = D / VEC;   // lanes per token
   constexpr int RPW = kWave / LPR;
   static_assert(LPR <= kWave && kWave % LPR == 0, "row split");
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int rg = lane / LPR;
   const int ch = lane % LPR;
   Item it;
-  if (!decode_item(p, (int64_t)blockIdx.x * kDecodeWaves + wave, it)) return;
+  if (!decode_item(p, (int64_t)blockIdx.x * kDecodeWaves + wave_id(), it)) return;
   const int G = p.group;
   const int hq0 = it.kvh * G;
 
@@ -341,11 +596,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_valu_kernel(const
     const int lb = tok / block_size;
     int phys = bt[lb];
     phys = (phys >= 0 && phys < p.num_blocks) ? phys : 0;
-    const int64_t off = (((int64_t)phys * p.num_kv_heads + it.kvh) * block_size +
-                         (tok - lb * block_size)) * D + ch * VEC;
+    const int64_t base = ((int64_t)phys * p.num_kv_heads + it.kvh) * block_size * D;
+    const int o = tok - lb * block_size;
     float kf[VEC], vf[VEC];
-    load_row(p.k_cache, off, kf);
-    load_row(p.v_cache, off, vf);
+    load_row(p.k_cache, base + ((int64_t)ch * block_size + o) * VEC, kf);  // granule ch
+    load_row(p.v_cache, base + (int64_t)o * D + ch * VEC, vf);
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
       if (h >= G) continue;
@@ -353,7 +608,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_valu_kernel(const
 #pragma unroll
       for (int e = 0; e < VEC; ++e) s = fmaf(q[h][e], kf[e], s);
 #pragma unroll
-      for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
+      for (int o2 = 1; o2 < LPR; o2 <<= 1) s += __shfl_xor(s, o2);
       const float x = s * p.scale_log2;
       const float mn = fmaxf(m[h], x);
       const float a = fast_exp2(m[h] - mn);
@@ -415,15 +670,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_valu_kernel(const
   }
 }
 
-// ---------------------------------------------------------------------------
-// cross-partition merge
-// ---------------------------------------------------------------------------
-//
 // One workgroup per (sequence, query head) with more than one partition:
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p acc_p / sum_p w_p l_p
 // Partitions are split over PG thread groups in a fixed interleave, then
 // summed in a fixed order through LDS: deterministic.
-
 constexpr int kReduceThreads = 256;
 
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float* scratch) {
@@ -451,8 +701,7 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
 
   const int64_t row = blockIdx.x;          // seq * Hq + h
   const int seq = (int)(row / p.num_q_heads);
-  int n = p.context_lens[seq];
-  n = min(max(n, 0), p.max_tokens);
+  const int n = clamp_ctx(p, seq);
   const int np = (n + p.partition - 1) / p.partition;
   if (np <= 1) return;                     // written directly by the decode kernel
   const int P = p.max_partitions;
@@ -497,9 +746,46 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   }
 }
 
+// ---------------------------------------------------------------------------
+// launch helpers
+// ---------------------------------------------------------------------------
+
+template <int D, int BS>
+hipError_t launch_streamk(const DecodeParams& p, hipStream_t stream) {
+  const int blocks = p.max_workers / kDecodeWaves;
+  const size_t lds = (size_t)(p.num_seqs + 1) * sizeof(int);
+  hipLaunchKernelGGL((decode_mfma_streamk_kernel<D, BS>), dim3(blocks),
+                     dim3(kDecodeWaves * kWave), lds, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_streamk_merge_kernel<D>), dim3(p.num_seqs * p.num_kv_heads),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_streamk_bs(const DecodeParams& p, int block_size, hipStream_t stream) {
+  switch (block_size) {
+    case 8: return launch_streamk<D, 8>(p, stream);
+    case 16: return launch_streamk<D, 16>(p, stream);
+    case 32: return launch_streamk<D, 32>(p, stream);
+    default: return launch_streamk<D, 64>(p, stream);
+  }
+}
+
 template <int D, int BS>
 void launch_mfma(const DecodeParams& p, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((decode_mfma_kernel<D, BS>), grid, dim3(kDecodeWaves * kWave), 0, stream, p);
+}
+
+template <int D>
+void launch_mfma_bs(const DecodeParams& p, int block_size, dim3 grid, hipStream_t stream) {
+  switch (block_size) {
+    case 8: launch_mfma<D, 8>(p, grid, stream); break;
+    case 16: launch_mfma<D, 16>(p, grid, stream); break;
+    case 32: launch_mfma<D, 32>(p, grid, stream); break;
+    default: launch_mfma<D, 64>(p, grid, stream); break;
+  }
 }
 
 template <typename T, int D>
@@ -517,32 +803,60 @@ void launch_valu(const DecodeParams& p, int block_size, dim3 grid, hipStream_t s
     hipLaunchKernelGGL((decode_valu_kernel<T, D, 16>), grid, dim3(kDecodeWaves * kWave), 0, stream, p, block_size);
 }
 
-template <int D>
-void launch_mfma_bs(const DecodeParams& p, int block_size, dim3 grid, hipStream_t stream) {
-  switch (block_size) {
-    case 8: launch_mfma<D, 8>(p, grid, stream); break;
-    case 16: launch_mfma<D, 16>(p, grid, stream); break;
-    case 32: launch_mfma<D, 32>(p, grid, stream); break;
-    default: launch_mfma<D, 64>(p, grid, stream); break;
-  }
-}
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-DecodeWorkspace decode_workspace(int num_seqs, int num_q_heads, int head_dim, int max_partitions) {
+int streamk_workers_per_cu(int head_dim) {
+  // All instantiations of one head_dim share the register footprint; the
+  // LDS of the largest supported batch is assumed.
+  int blocks = 0;
+  const size_t lds = (size_t)(kStreamKMaxSeqs + 1) * sizeof(int);
+  hipError_t e = head_dim == 128
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma_streamk_kernel<128, 16>,
+                                                     kDecodeWaves * kWave, lds)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma_streamk_kernel<64, 16>,
+                                                     kDecodeWaves * kWave, lds);
+  if (e != hipSuccess || blocks <= 0) return -1;
+  return blocks * kDecodeWaves;
+}
+
+DecodePath decode_path(int num_seqs, pa_dtype dtype, int partition_size, bool vector_only) {
+  if (dtype == PA_BF16 && !vector_only && partition_size == 0 && num_seqs <= kStreamKMaxSeqs)
+    return DecodePath::kStreamK;
+  return DecodePath::kPartition;
+}
+
+DecodeWorkspace decode_workspace_partition(int num_seqs, int num_q_heads, int head_dim,
+                                           int max_partitions) {
   DecodeWorkspace w{};
   if (max_partitions <= 1) return w;
   const size_t rows = (size_t)num_seqs * num_q_heads * max_partitions;
-  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   w.m_off = 0;
-  w.l_off = align(rows * sizeof(float));
-  w.acc_off = w.l_off + align(rows * sizeof(float));
-  w.total = w.acc_off + align(rows * head_dim * sizeof(float));
+  w.l_off = align256(rows * sizeof(float));
+  w.acc_off = w.l_off + align256(rows * sizeof(float));
+  w.total = w.acc_off + align256(rows * head_dim * sizeof(float));
+  return w;
+}
+
+DecodeWorkspace decode_workspace_streamk(int num_seqs, int group, int head_dim) {
+  DecodeWorkspace w{};
+  const size_t slots = (size_t)kStreamKMaxWorkers * 2 * group;
+  w.header_off = 0;
+  w.prefix_off = 256;
+  w.m_off = w.prefix_off + align256((size_t)(num_seqs + 1) * sizeof(int));
+  w.l_off = w.m_off + align256(slots * sizeof(float));
+  w.acc_off = w.l_off + align256(slots * sizeof(float));
+  w.total = w.acc_off + align256(slots * head_dim * sizeof(float));
   return w;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, pa_dtype dtype,
-                         bool vector_only, hipStream_t stream) {
+                         bool vector_only, DecodePath path, hipStream_t stream) {
+  if (path == DecodePath::kStreamK) {
+    return head_dim == 128 ? launch_streamk_bs<128>(p, block_size, stream)
+                           : launch_streamk_bs<64>(p, block_size, stream);
+  }
   const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads * p.max_partitions;
   if (items == 0) return hipSuccess;
   const dim3 grid((unsigned)((items + kDecodeWaves - 1) / kDecodeWaves));

@@ -33,29 +33,48 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_m;        // [S][Hq][P]    running maxima, log2 domain
-  float* ws_l;        // [S][Hq][P]    running sums
-  float* ws_acc;      // [S][Hq][P][D] unnormalised outputs
+  // fixed-partition path: partials [S][Hq][P] (m, l) and [S][Hq][P][D] (acc)
+  // stream-K path: partials [W][2][G] (m, l) and [W][2][G][D] (acc)
+  float* ws_m;        // running maxima (log2 domain; the reference point of l and acc)
+  float* ws_l;        // running sums
+  float* ws_acc;      // unnormalised outputs
+  int32_t* ws_prefix; // stream-K: [S+1] tile prefix over sequences, written by the decode kernel
+  int64_t* ws_header; // stream-K: {total tiles T, workers W}, written by the decode kernel
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
   int group;          // num_q_heads / num_kv_heads
   int num_blocks;
   int max_blocks_per_seq;
-  int partition;      // tokens per partition
-  int max_partitions; // P = ceil(max_context_len / partition)
-  int max_tokens;     // min(max_blocks_per_seq * block_size, P * partition): every
-                      // context length is clamped to it, so no index leaves its buffer
+  int partition;      // fixed-partition path: tokens per partition
+  int max_partitions; // fixed-partition path: P = ceil(max_context_len / partition)
+  int max_tokens;     // every context length is clamped to it, so no index leaves its buffer
+  int max_workers;    // stream-K path: waves launched (slot capacity of the workspace)
   float scale_log2;   // scale * log2(e)
 };
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, pa_dtype dtype,
-                         bool vector_only, hipStream_t stream);
+// Stream-K decomposition limits.
+constexpr int kStreamKMaxSeqs = 8192;     // per-sequence prefix kept in LDS
+constexpr int kStreamKMaxWorkers = 2048;  // workspace slots (256 CUs x 8 resident waves)
+constexpr int kStreamKMinTiles = 8;       // a worker gets at least this many 16-token tiles
 
-// Workspace offsets (bytes) for the decode partials; shared by size query and launch.
+enum class DecodePath { kStreamK, kPartition };
+
+// Resident waves per CU of the stream-K kernel for head_dim (-1 on error).
+int streamk_workers_per_cu(int head_dim);
+
+// Which path pa_decode_attention takes (host rule shared with the size query).
+DecodePath decode_path(int num_seqs, pa_dtype dtype, int partition_size, bool vector_only);
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, pa_dtype dtype,
+                         bool vector_only, DecodePath path, hipStream_t stream);
+
+// Workspace offsets (bytes); shared by the size query and the launch.
 struct DecodeWorkspace {
-  size_t m_off, l_off, acc_off, total;
+  size_t m_off, l_off, acc_off, prefix_off, header_off, total;
 };
-DecodeWorkspace decode_workspace(int num_seqs, int num_q_heads, int head_dim, int max_partitions);
+DecodeWorkspace decode_workspace_partition(int num_seqs, int num_q_heads, int head_dim,
+                                           int max_partitions);
+DecodeWorkspace decode_workspace_streamk(int num_seqs, int group, int head_dim);
 
 }  // namespace pa

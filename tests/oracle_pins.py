@@ -12,9 +12,11 @@ disagrees with:
   large scale);
 * the sharing and copy-on-write invariants.
 
-The pool construction below restates the layout reading (pool
-``[NB][Hkv][bs][D]``, token p of a sequence in block ``table[p // bs]`` at
-offset ``p % bs``) independently of the oracle's own code.
+The pool construction below restates the layout reading independently of the
+oracle's own code: token p of a sequence lives in block ``table[p // bs]`` at
+offset ``o = p % bs``; V element d of it is ``V[blk][h][o][d]``, K element d is
+``K[blk][h][d // x][o][d % x]`` (granules of x elements; the GPU library uses
+16-byte granules, the oracle accepts any x that divides D).
 """
 
 from __future__ import annotations
@@ -63,11 +65,16 @@ def nan_like_pool(shape, dtype):
     return np.full(shape, np.nan, dtype=np.float32)
 
 
-def build_pool(k_logical, v_logical, tables, num_blocks, block_size, dtype):
+def k_pool_shape(nb, hkv, bs, d, x):
+    return (nb, hkv, d // x, bs, x)
+
+
+def build_pool(k_logical, v_logical, tables, num_blocks, block_size, dtype, x=1):
     """Scatter per-sequence logical K/V ``[ctx][Hkv][D]`` into NaN pools by
     explicit loops over tokens, heads and dims."""
     hkv, d = k_logical[0].shape[1], k_logical[0].shape[2]
-    kp = nan_like_pool((num_blocks, hkv, block_size, d), dtype)
+    assert d % x == 0
+    kp = nan_like_pool(k_pool_shape(num_blocks, hkv, block_size, d, x), dtype)
     vp = nan_like_pool((num_blocks, hkv, block_size, d), dtype)
     for i, (ks, vs) in enumerate(zip(k_logical, v_logical)):
         for p in range(ks.shape[0]):
@@ -75,7 +82,7 @@ def build_pool(k_logical, v_logical, tables, num_blocks, block_size, dtype):
             off = p % block_size
             for g in range(hkv):
                 for e in range(d):
-                    kp[blk, g, off, e] = ks[p, g, e]
+                    kp[blk, g, e // x, off, e % x] = ks[p, g, e]
                     vp[blk, g, off, e] = vs[p, g, e]
     return kp, vp
 
@@ -107,7 +114,7 @@ def dense_attention_loops(q, k_logical, v_logical, scale, dtype):
     return out
 
 
-def random_case(rng, *, num_seqs, hq, hkv, d, bs, ctx_max, dtype, slack=3, ctx=None):
+def random_case(rng, *, num_seqs, hq, hkv, d, bs, ctx_max, dtype, slack=3, ctx=None, x=1):
     """Logical K/V per sequence, a random non-sharing table over a shuffled
     pool, and Q.  Returns everything the oracle and brute force need."""
     if ctx is None:
@@ -124,9 +131,9 @@ def random_case(rng, *, num_seqs, hq, hkv, d, bs, ctx_max, dtype, slack=3, ctx=N
     k_logical = [random_values(rng, (c, hkv, d), dtype) for c in ctx]
     v_logical = [random_values(rng, (c, hkv, d), dtype) for c in ctx]
     q = random_values(rng, (num_seqs, hq, d), dtype)
-    kp, vp = build_pool(k_logical, v_logical, tables, nb, bs, dtype)
+    kp, vp = build_pool(k_logical, v_logical, tables, nb, bs, dtype, x=x)
     return dict(q=q, kp=kp, vp=vp, tables=tables, ctx=np.array(ctx, dtype=np.int32),
-                k_logical=k_logical, v_logical=v_logical, nb=nb, bs=bs, dtype=dtype)
+                k_logical=k_logical, v_logical=v_logical, nb=nb, bs=bs, dtype=dtype, x=x)
 
 
 # ---------------------------------------------------------------------------
@@ -194,9 +201,9 @@ def pin_slot_bijection(O):
 
 def pin_write_bruteforce(O):
     rng = np.random.default_rng(11)
-    for dtype in ("f32", "bf16"):
-        nb, hkv, bs, d, t = 6, 3, 4, 5, 9
-        kp = random_values(rng, (nb, hkv, bs, d), dtype)
+    for dtype, d, x in (("f32", 5, 1), ("bf16", 6, 3), ("bf16", 8, 8), ("f32", 4, 2)):
+        nb, hkv, bs, t = 6, 3, 4, 9
+        kp = random_values(rng, k_pool_shape(nb, hkv, bs, d, x), dtype)
         vp = random_values(rng, (nb, hkv, bs, d), dtype)
         kn = random_values(rng, (t, hkv, d), dtype)
         vn = random_values(rng, (t, hkv, d), dtype)
@@ -211,7 +218,7 @@ def pin_write_bruteforce(O):
             blk, off = int(slots[j]) // bs, int(slots[j]) % bs
             for g in range(hkv):
                 for e in range(d):
-                    ek[blk, g, off, e] = kn[j, g, e]
+                    ek[blk, g, e // x, off, e % x] = kn[j, g, e]
                     ev[blk, g, off, e] = vn[j, g, e]
         assert k2.tobytes() == ek.tobytes() and v2.tobytes() == ev.tobytes()
         # inputs are not modified in place
@@ -223,8 +230,8 @@ def pin_write_roundtrip(O):
     through the same table, returns the written vectors bit for bit; every
     other slot keeps its sentinel."""
     rng = np.random.default_rng(12)
-    c = random_case(rng, num_seqs=3, hq=2, hkv=2, d=3, bs=4, ctx_max=13, dtype="bf16",
-                    ctx=[13, 0, 6])
+    c = random_case(rng, num_seqs=3, hq=2, hkv=2, d=4, bs=4, ctx_max=13, dtype="bf16",
+                    ctx=[13, 0, 6], x=2)
     kp, vp = nan_like_pool(c["kp"].shape, "bf16"), nan_like_pool(c["vp"].shape, "bf16")
     seq_ids = np.concatenate([np.full(n, i, np.int32) for i, n in enumerate(c["ctx"])])
     pos = np.concatenate([np.arange(n, dtype=np.int32) for n in c["ctx"]])
@@ -238,7 +245,7 @@ def pin_write_roundtrip(O):
 def pin_copy(O):
     rng = np.random.default_rng(13)
     nb, hkv, bs, d = 8, 2, 4, 3
-    kp = random_values(rng, (nb, hkv, bs, d), "bf16")
+    kp = random_values(rng, k_pool_shape(nb, hkv, bs, d, 1), "bf16")
     vp = random_values(rng, (nb, hkv, bs, d), "bf16")
     pairs = np.array([[1, 5], [1, 6], [3, 0]], dtype=np.int32)
     k2, v2 = O.copy_blocks(kp, vp, pairs)
@@ -255,34 +262,37 @@ def pin_copy(O):
 
 
 DENSE_CASES = [
-    # (num_seqs, hq, hkv, d, bs, ctx_max, dtype, seed)
-    (3, 4, 2, 4, 4, 30, "f32", 1),
-    (2, 4, 1, 3, 3, 20, "bf16", 2),
-    (2, 2, 2, 5, 1, 9, "f32", 3),
-    (3, 6, 3, 2, 8, 40, "bf16", 4),
-    (1, 8, 2, 4, 16, 37, "bf16", 5),
-    (4, 1, 1, 6, 2, 11, "f32", 6),
+    # (num_seqs, hq, hkv, d, bs, ctx_max, dtype, seed, x)
+    (3, 4, 2, 4, 4, 30, "f32", 1, 2),
+    (2, 4, 1, 3, 3, 20, "bf16", 2, 1),
+    (2, 2, 2, 5, 1, 9, "f32", 3, 5),
+    (3, 6, 3, 2, 8, 40, "bf16", 4, 1),
+    (1, 8, 2, 4, 16, 37, "bf16", 5, 4),
+    (4, 1, 1, 6, 2, 11, "f32", 6, 3),
+    (2, 4, 2, 8, 4, 19, "bf16", 7, 2),
 ]
 
 
 def pin_attention_dense(O, cases=DENSE_CASES, tol=1e-12):
-    for (s_n, hq, hkv, d, bs, cmax, dtype, seed) in cases:
+    for (s_n, hq, hkv, d, bs, cmax, dtype, seed, x) in cases:
         rng = np.random.default_rng(100 + seed)
-        c = random_case(rng, num_seqs=s_n, hq=hq, hkv=hkv, d=d, bs=bs, ctx_max=cmax, dtype=dtype)
+        c = random_case(rng, num_seqs=s_n, hq=hq, hkv=hkv, d=d, bs=bs, ctx_max=cmax, dtype=dtype,
+                        x=x)
         scale = float(np.float32(1 / math.sqrt(d)))
         got = O.decode_attention(c["q"], c["kp"], c["vp"], c["tables"], c["ctx"], scale, dtype)
         want = dense_attention_loops(c["q"], c["k_logical"], c["v_logical"], scale, dtype)
         err = np.max(np.abs(got - want)) if got.size else 0.0
-        assert err <= tol, (s_n, hq, hkv, d, bs, dtype, err)
+        assert err <= tol, (s_n, hq, hkv, d, bs, dtype, x, err)
 
 
 def pin_attention_sdpa(O):
     import torch
     rng = np.random.default_rng(21)
-    for (hq, hkv, d, n, dtype) in ((8, 2, 16, 37, "bf16"), (4, 4, 8, 5, "f32"), (6, 1, 4, 64, "f32")):
+    for (hq, hkv, d, n, dtype, x) in ((8, 2, 16, 37, "bf16", 8), (4, 4, 8, 5, "f32", 4),
+                                      (6, 1, 4, 64, "f32", 1)):
         bs = n  # identity table, one block holds the whole context
         c = random_case(rng, num_seqs=1, hq=hq, hkv=hkv, d=d, bs=bs, ctx_max=n, dtype=dtype,
-                        ctx=[n], slack=0)
+                        ctx=[n], slack=0, x=x)
         scale = float(np.float32(0.37))
         got = O.decode_attention(c["q"], c["kp"], c["vp"], c["tables"], c["ctx"], scale, dtype)
         conv = (lambda a: np.vectorize(bf16_bits_to_float)(a)) if dtype == "bf16" else (lambda a: a.astype(np.float64))
@@ -304,7 +314,7 @@ def _single(O, q, ks, vs, scale, bs=4, dtype="f32"):
     perm = rng.permutation(nb)
     table = np.full((1, max(1, -(-n // bs))), -1, np.int32)
     table[0, :-(-n // bs)] = perm[:-(-n // bs)]
-    kp, vp = build_pool([ks], [vs], table, nb, bs, dtype)
+    kp, vp = build_pool([ks], [vs], table, nb, bs, dtype, x=2 if ks.shape[2] % 2 == 0 else 1)
     return O.decode_attention(q, kp, vp, table, np.array([n], np.int32), scale, dtype)[0, 0]
 
 
@@ -367,7 +377,7 @@ def pin_shared_vs_private(O):
     for i, n in enumerate(nblk):
         t_priv[i, :n] = perm[cur:cur + n]
         cur += n
-    kp1, vp1 = build_pool(ks, vs, t_priv, nb_priv, bs, "bf16")
+    kp1, vp1 = build_pool(ks, vs, t_priv, nb_priv, bs, "bf16", x=3)
     # shared layout: the full prefix blocks are stored once
     nb_sh = npre + sum(n - npre for n in nblk)
     perm = rng.permutation(nb_sh)
@@ -378,7 +388,7 @@ def pin_shared_vs_private(O):
         t_sh[i, :npre] = shared
         t_sh[i, npre:n] = perm[cur:cur + n - npre]
         cur += n - npre
-    kp2, vp2 = build_pool(ks, vs, t_sh, nb_sh, bs, "bf16")
+    kp2, vp2 = build_pool(ks, vs, t_sh, nb_sh, bs, "bf16", x=3)
     assert nb_sh < nb_priv
     o1 = O.decode_attention(q, kp1, vp1, t_priv, ctx, 0.5, "bf16")
     o2 = O.decode_attention(q, kp2, vp2, t_sh, ctx, 0.5, "bf16")
@@ -396,7 +406,7 @@ def pin_cow_isolation(O):
     nb = 6
     table = np.full((samples, 2), -1, np.int32)
     table[:, 0], table[:, 1] = 2, 4
-    kp, vp = build_pool([ks], [vs], table[:1], nb, bs, "bf16")
+    kp, vp = build_pool([ks], [vs], table[:1], nb, bs, "bf16", x=2)
     q = random_values(rng, (samples, hq, d), "bf16")
     ctx = np.full(samples, ctx0, np.int32)
     before = O.decode_attention(q, kp, vp, table, ctx, 0.5, "bf16")

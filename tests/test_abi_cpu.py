@@ -79,12 +79,19 @@ def test_decode_validation(lib):
     assert _decode(lib, max_ctx=-3) == SHAPE
     assert _decode(lib, scale=float("nan")) == SHAPE
     assert _decode(lib, flags=2) == UNSUP
-    assert _decode(lib, out=NULL) == NUL
-    assert _decode(lib, ctx=NULL) == NUL
-    assert _decode(lib, q=MISALIGNED) == UNSUP
+    # fixed partition of 64 tokens, one partition: no workspace needed
+    assert _decode(lib, part=64, out=NULL) == NUL
+    assert _decode(lib, part=64, ctx=NULL) == NUL
+    assert _decode(lib, part=64, q=MISALIGNED) == UNSUP
+    # stream-K (the default for bf16): with its workspace, the same checks
+    big = lib.pa_decode_workspace_size(2, 8, 2, 128, 16, 40, 0, 1, 0)
+    assert big > 0
+    assert _decode(lib, out=NULL, ws=FAKE, ws_bytes=big) == NUL
+    assert _decode(lib, k=MISALIGNED, ws=FAKE, ws_bytes=big) == UNSUP
+    assert _decode(lib, ws=FAKE, ws_bytes=big - 1) == WS
     # two partitions need a workspace
     assert _decode(lib, part=16, max_ctx=40) == WS
-    need = lib.pa_decode_workspace_size(2, 8, 2, 128, 16, 40, 16)
+    need = lib.pa_decode_workspace_size(2, 8, 2, 128, 16, 40, 16, 1, 0)
     assert need > 0
     assert _decode(lib, part=16, ws=FAKE, ws_bytes=need - 1) == WS
     assert _decode(lib, part=16, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == WS   # alignment
@@ -99,13 +106,25 @@ def test_workspace_and_partition_rules(lib):
     assert pa.decode_partition_size(4, 4, 16, 40) == 64
     assert pa.decode_partition_size(4, 8, 32, 131072, 512) == 512
     assert pa.decode_partition_size(4, 8, 32, 131072, 500) == 0
-    # single partition -> no workspace
-    assert pa.decode_workspace_size(4, 4, 4, 64, 16, 40) == 0
+    import torch
+    f32 = torch.float32
+    # fixed partitions: single partition -> no workspace
+    assert pa.decode_workspace_size(4, 4, 4, 64, 16, 40, dtype=f32) == 0
     # P partitions: (m, l) and acc float32 rows, each region 256-byte aligned
     s, hq, d, p = 4, 64, 128, 256
     rows = s * hq * p
     al = lambda x: (x + 255) // 256 * 256
     assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072, 512) == al(rows * 4) * 2 + al(rows * d * 4)
+    assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072, 0, dtype=f32) == \
+        pa.decode_workspace_size(s, hq, 8, d, 32, 131072, 1024)
+    # stream-K (bf16, library choice): header, prefix, then 2048 waves x 2 slots x G heads
+    g = 8
+    slots = 2048 * 2 * g
+    want = 256 + al((s + 1) * 4) + 2 * al(slots * 4) + al(slots * d * 4)
+    assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072) == want
+    assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072, vector_only=True) == \
+        pa.decode_workspace_size(s, hq, 8, d, 32, 131072, dtype=f32)
+    assert _decode(lib, ws=FAKE, ws_bytes=0) == WS        # stream-K always needs its workspace
 
 
 def test_write_copy_slots_validation(lib):

@@ -139,9 +139,6 @@ def test_max_context_len_upper_bound_is_harmless():
     dev.run_setup()
     a = dev.run_step().clone()
     dev.max_ctx = wl.max_context_len * 3 + 17
-    need = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                    wl.block_size, dev.max_ctx, 0)
-    dev.workspace = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
     b = dev.run_step()
     torch.cuda.synchronize()
     _, _, ref, _ = run_oracle(wl, wl.setup + wl.step)

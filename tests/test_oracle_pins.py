@@ -26,14 +26,16 @@ def test_pin(pin):
 @given(num_seqs=st.integers(1, 3), hkv=st.integers(1, 2), grp=st.sampled_from([1, 2, 4]),
        d=st.integers(1, 5), bs=st.sampled_from([1, 2, 3, 4, 8, 16, 32, 64]),
        ctx_max=st.integers(0, 45), dtype=st.sampled_from(["f32", "bf16"]),
-       seed=st.integers(0, 2**31 - 1))
+       seed=st.integers(0, 2**31 - 1), xsel=st.integers(0, 3))
 def test_paged_equals_dense_any_block_size_and_permutation(num_seqs, hkv, grp, d, bs, ctx_max,
-                                                           dtype, seed):
+                                                           dtype, seed, xsel):
     """Invariant (a): paging changes placement only -- the oracle equals
     brute-force dense attention for any block size and any physical order."""
     rng = np.random.default_rng(seed)
+    divisors = [x for x in range(1, d + 1) if d % x == 0]
+    x = divisors[xsel % len(divisors)]
     c = P.random_case(rng, num_seqs=num_seqs, hq=hkv * grp, hkv=hkv, d=d, bs=bs,
-                      ctx_max=ctx_max, dtype=dtype)
+                      ctx_max=ctx_max, dtype=dtype, x=x)
     scale = float(np.float32(1 / math.sqrt(d)))
     got = real.decode_attention(c["q"], c["kp"], c["vp"], c["tables"], c["ctx"], scale, dtype)
     want = P.dense_attention_loops(c["q"], c["k_logical"], c["v_logical"], scale, dtype)
@@ -45,7 +47,7 @@ def test_placement_invariance_bitwise():
     bit-identical oracle outputs."""
     rng = np.random.default_rng(5)
     c = P.random_case(rng, num_seqs=3, hq=4, hkv=2, d=4, bs=4, ctx_max=30, dtype="bf16",
-                      ctx=[30, 7, 12])
+                      ctx=[30, 7, 12], x=2)
     rng2 = np.random.default_rng(6)
     nb = c["nb"] + 4
     perm = rng2.permutation(nb)
@@ -55,7 +57,7 @@ def test_placement_invariance_bitwise():
         k = -(-int(n) // 4)
         t2[i, :k] = perm[cur:cur + k]
         cur += k
-    kp2, vp2 = P.build_pool(c["k_logical"], c["v_logical"], t2, nb, 4, "bf16")
+    kp2, vp2 = P.build_pool(c["k_logical"], c["v_logical"], t2, nb, 4, "bf16", x=2)
     o1 = real.decode_attention(c["q"], c["kp"], c["vp"], c["tables"], c["ctx"], 0.3, "bf16")
     o2 = real.decode_attention(c["q"], kp2, vp2, t2, c["ctx"], 0.3, "bf16")
     assert o1.tobytes() == o2.tobytes()
@@ -69,13 +71,17 @@ def test_zero_context_gives_zeros_and_unused_entries_never_read():
 
 
 def test_contract_errors_raise():
-    kp = np.zeros((4, 1, 2, 1), np.float32)
+    kp = np.zeros((4, 1, 1, 2, 1), np.float32)
+    vp = np.zeros((4, 1, 2, 1), np.float32)
     with pytest.raises(oracle.paged_attention.ContractError):
-        real.write_kv(kp, kp, np.zeros((2, 1, 1), np.float32), np.zeros((2, 1, 1), np.float32),
+        real.write_kv(kp, vp, np.zeros((2, 1, 1), np.float32), np.zeros((2, 1, 1), np.float32),
                       np.array([3, 3]))
     with pytest.raises(oracle.paged_attention.ContractError):
-        real.write_kv(kp, kp, np.zeros((1, 1, 1), np.float32), np.zeros((1, 1, 1), np.float32),
+        real.write_kv(kp, vp, np.zeros((1, 1, 1), np.float32), np.zeros((1, 1, 1), np.float32),
                       np.array([8]))
+    with pytest.raises(oracle.paged_attention.ContractError):
+        real.write_kv(vp, vp, np.zeros((1, 1, 1), np.float32), np.zeros((1, 1, 1), np.float32),
+                      np.array([1]))                                     # K pool not granular
     t = np.array([[0, -1]], np.int32)
     with pytest.raises(oracle.paged_attention.ContractError):
         real.slot_mapping(t, np.array([0]), np.array([2]), 2, 4)     # entry -1
@@ -84,10 +90,10 @@ def test_contract_errors_raise():
     with pytest.raises(oracle.paged_attention.ContractError):
         real.slot_mapping(t, np.array([1]), np.array([0]), 2, 4)     # no such sequence
     with pytest.raises(oracle.paged_attention.ContractError):
-        kp2 = np.zeros((4, 2, 2, 1), np.float32)                    # Hq=3 vs Hkv=2
-        real.decode_attention(np.zeros((1, 3, 1), np.float32), kp2, kp2, t, np.array([1]), 1.0, "f32")
+        kp2, vp2 = np.zeros((4, 2, 1, 2, 1), np.float32), np.zeros((4, 2, 2, 1), np.float32)
+        real.decode_attention(np.zeros((1, 3, 1), np.float32), kp2, vp2, t, np.array([1]), 1.0, "f32")
     with pytest.raises(oracle.paged_attention.ContractError):
-        real.decode_attention(np.zeros((1, 1, 1), np.float32), kp, kp, t, np.array([3]), 1.0, "f32")
+        real.decode_attention(np.zeros((1, 1, 1), np.float32), kp, vp, t, np.array([3]), 1.0, "f32")
 
 
 # ---------------------------------------------------------------------------
@@ -107,8 +113,14 @@ MUTATIONS = {
     "transposed-operand": ("(w @ v_t) / w.sum()", "(w @ k_t) / w.sum()"),
     "bf16-shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "slot-no-offset": ("* block_size + _offset_in_block(p, block_size)", "* block_size"),
-    "write-k-gets-v": ("k_out[b, :, o, :] = k_new[j]", "k_out[b, :, o, :] = v_new[j]"),
+    "write-k-gets-v": ("= k_new[j].reshape(num_kv_heads, head_dim // x, x)",
+                       "= v_new[j].reshape(num_kv_heads, head_dim // x, x)"),
     "write-swapped-divmod": ("b, o = divmod(int(s), block_size)", "o, b = divmod(int(s), block_size)"),
+    "granule-order-swapped": ("return g.reshape(g.shape[0], -1)",
+                              "return g.transpose(0, 2, 1).reshape(g.shape[0], -1)"),
+    "write-granule-order-swapped": (
+        "k_new[j].reshape(num_kv_heads, head_dim // x, x)",
+        "k_new[j].reshape(num_kv_heads, x, head_dim // x).transpose(0, 2, 1)"),
     "copy-reversed": ("k_out[d] = k_pool[s]", "k_out[s] = k_pool[d]"),
     "scale-not-float32": ("np.float64(np.float32(scale))", "np.float64(scale) * 1.001"),
 }

@@ -67,6 +67,11 @@ def elem_bytes(dtype: str) -> int:
     return 2 if dtype == BF16 else 4
 
 
+def granule(dtype: str) -> int:
+    """Elements per 16-byte granule of the K pool layout."""
+    return 16 // elem_bytes(dtype)
+
+
 # ---------------------------------------------------------------------------
 # plan containers
 # ---------------------------------------------------------------------------
@@ -112,8 +117,12 @@ class Workload:
         return int(self.context_lens.max()) if self.num_seqs else 0
 
     def empty_pools(self):
-        shape = (self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim)
-        return nan_pool(shape, self.dtype), nan_pool(shape, self.dtype)
+        """NaN-filled K pool [NB][Hkv][D/x][bs][x] (x = 16-byte granule) and
+        V pool [NB][Hkv][bs][D]."""
+        x = granule(self.dtype)
+        kshape = (self.num_blocks, self.num_kv_heads, self.head_dim // x, self.block_size, x)
+        vshape = (self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim)
+        return nan_pool(kshape, self.dtype), nan_pool(vshape, self.dtype)
 
     # --- accounting (algorithmic bytes of one decode step) -----------------
     def kv_bytes_read(self) -> int:

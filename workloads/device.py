@@ -45,10 +45,9 @@ class DeviceWorkload:
         self.out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32,
                                device=device)
         self.max_ctx = wl.max_context_len
-        need = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
-                                        wl.head_dim, wl.block_size, self.max_ctx,
-                                        wl.partition_size)
-        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        self.torch_dtype = torch.bfloat16 if wl.dtype == BF16 else torch.float32
+        self.workspace = torch.empty(1, dtype=torch.uint8, device=device)
+        self._ensure_workspace(wl.partition_size, False)
         self.setup_ops = [self._upload(op) for op in wl.setup]
         self.step_ops = [self._upload(op) for op in wl.step]
 
@@ -68,6 +67,15 @@ class DeviceWorkload:
             return ("decode", x)
         raise ValueError(kind)
 
+    def _ensure_workspace(self, partition_size, vector_only):
+        wl = self.wl
+        need = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
+                                        wl.head_dim, wl.block_size, self.max_ctx,
+                                        partition_size, self.torch_dtype, vector_only)
+        if need > self.workspace.numel():
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self.workspace
+
     # -------------------------------------------------------------------
     def _run(self, ops, pool=0, partition_size=None, vector_only=False, stream=None):
         wl = self.wl
@@ -82,12 +90,7 @@ class DeviceWorkload:
             elif kind == "copy":
                 pa.copy_blocks(k, v, x, stream=stream)
             else:
-                ws = self.workspace
-                if part != wl.partition_size:
-                    need = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
-                                                    wl.head_dim, wl.block_size, self.max_ctx, part)
-                    if need > ws.numel():
-                        ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+                ws = self._ensure_workspace(part, vector_only)
                 pa.decode_attention(self.q, k, v, self.tables[x], self.ctx, wl.scale, self.max_ctx,
                                     partition_size=part, workspace=ws, out=self.out,
                                     vector_only=vector_only, stream=stream)
