@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition", type=int, default=None,
                     help="decode partition size (default: the workload's / the library's choice)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run pa_copy_blocks over a known number of bytes (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -86,8 +89,31 @@ def cpu_baseline(wl, budget_s):
     }
 
 
+def calibrate_copy(steps):
+    """Copy 8192 blocks of 32 KiB in each of the K and V pools: 256 MiB read
+    and 256 MiB written per launch, with no reuse between launches."""
+    import torch
+
+    import paged_kv_cache_188_amd as pa
+    nb, hkv, bs, d = 16384, 8, 16, 128
+    k = torch.zeros((nb, hkv, d // 8, bs, 8), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((nb, hkv, bs, d), dtype=torch.bfloat16, device="cuda")
+    half = nb // 2
+    pairs = torch.stack([torch.arange(half), torch.arange(half) + half], 1).to(torch.int32).cuda()
+    for _ in range(steps):
+        pa.copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    block_bytes = hkv * bs * d * 2
+    print(json.dumps({"calibration": "pa_copy_blocks", "launches": steps,
+                      "read_bytes_per_launch": 2 * half * block_bytes,
+                      "write_bytes_per_launch": 2 * half * block_bytes}), flush=True)
+
+
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(each sequence's blocks live on one GPU; see the design notes). "

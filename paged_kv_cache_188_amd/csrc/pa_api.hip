@@ -157,7 +157,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
       !supported_head_dim(head_dim) || !valid_dtype(dtype) || num_seqs <= 0)
     return 0;  // invalid arguments, or no sequence: nothing to hold
   const bool vector_only = (flags & PA_DECODE_VECTOR_ONLY) != 0;
-  if (pa::decode_path(num_seqs, dtype, partition_size, vector_only) == pa::DecodePath::kStreamK)
+  if (pa::decode_path(num_seqs, block_size, dtype, partition_size, vector_only) ==
+      pa::DecodePath::kStreamK)
     return pa::decode_workspace_streamk(num_seqs, num_q_heads / num_kv_heads, head_dim).total;
   const int32_t part = pa_decode_partition_size(num_seqs, num_kv_heads, block_size,
                                                 max_context_len, partition_size);
@@ -185,7 +186,8 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, co
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
   const int32_t max_tokens = max_blocks_per_seq * block_size;
   const bool vector_only = (flags & PA_DECODE_VECTOR_ONLY) != 0;
-  const pa::DecodePath path = pa::decode_path(num_seqs, dtype, partition_size, vector_only);
+  const pa::DecodePath path =
+      pa::decode_path(num_seqs, block_size, dtype, partition_size, vector_only);
   // Same partition, partition count and workspace as pa_decode_workspace_size.
   const int32_t part = partition_size ? partition_size
                                       : choose_partition(num_seqs, num_kv_heads, block_size,
@@ -215,10 +217,8 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, co
     p.ws_m = reinterpret_cast<float*>(wsb + ws.m_off);
     p.ws_l = reinterpret_cast<float*>(wsb + ws.l_off);
     p.ws_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
-    if (path == pa::DecodePath::kStreamK) {
-      p.ws_prefix = reinterpret_cast<int32_t*>(wsb + ws.prefix_off);
-      p.ws_header = reinterpret_cast<int64_t*>(wsb + ws.header_off);
-    }
+    if (path == pa::DecodePath::kStreamK)
+      p.ws_handoff = reinterpret_cast<int32_t*>(wsb + ws.handoff_off);
   }
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;

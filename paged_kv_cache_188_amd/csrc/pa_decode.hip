@@ -17,8 +17,9 @@
 //     wave streams the same number of bytes whatever the length mix.  A wave
 //     writes the final output of every segment it covers whole and a float32
 //     partial (running max, running sum, unnormalised output) for at most two
-//     segments it shares with its neighbours; decode_streamk_merge_kernel
-//     combines those (log-sum-exp rescale, fixed order).
+//     segments it shares with its neighbours; the first wave of a shared
+//     segment records it, and decode_streamk_merge_kernel combines the
+//     partials (log-sum-exp rescale, fixed order).
 //   * fixed-partition path (float32 K/V, an explicit partition size, or very
 //     large batches): one wave per (segment, partition) work item, partials
 //     merged by decode_reduce_kernel.
@@ -129,26 +130,107 @@ __device__ __forceinline__ void mfma_load_q(const DecodeParams& p, int seq, int 
   }
 }
 
+template <int D>
+using VRowT = typename std::conditional<D / 16 == 8, uint4, uint2>::type;
+
+// One 16-token tile in registers.
+template <int D>
+struct Tile {
+  uint4 k[D / 32];  // key `col`, granule 4*s + grp (dims 32*s + 8*grp .. +7)
+  VRowT<D> v[4];    // value row 4*grp + j, dims (D/16)*col .. +D/16-1
+};
+
+// Load a tile whose 16 tokens lie in one block (BS >= 16): cb is the element
+// offset of the (block, KV head) chunk, o the tile's first token in the
+// block.  `past` marks a refill beyond the last tile: every lane of a load
+// instruction then reads the same granule at the chunk's start (one cache
+// line per instruction; distinct granules per instruction, so the compiler
+// cannot fold the loads into one and copy it) and the data is never used.
+template <int D, int BS>
+__device__ __forceinline__ void load_tile(const uint16_t* kpool, const uint16_t* vpool, int64_t cb,
+                                          int o, bool past, int lane, Tile<D>& b) {
+  constexpr int DV = D / 16;
+  const int grp = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+    b.k[s] = load_stream(reinterpret_cast<const uint4*>(
+        kpool + cb + (past ? 8 * s : ((int64_t)(4 * s + grp) * BS + o + col) * 8)));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    b.v[j] = load_stream(reinterpret_cast<const VRowT<D>*>(
+        vpool + cb + (past ? 8 * j : (int64_t)(o + 4 * grp + j) * D + DV * col)));
+}
+
+// Attend the G heads to one tile: `valid` (1..16) of its tokens are in the
+// context.  The running max is moved only when a score exceeds it by more
+// than kLazyMax, so every weight 2^(x - m_run) stays <= 2^kLazyMax and the
+// common path needs no cross-lane traffic; results are exact either way
+// (partials carry m_run as their reference point).
+template <int D>
+__device__ __forceinline__ void compute_tile(const DecodeParams& p, MfmaState<D>& st,
+                                             const bf16x8_t (&qv)[D / 32], Tile<D>& b, int valid,
+                                             int lane) {
+  constexpr int DV = D / 16;
+  const int grp = lane >> 4;
+  // scores: lane holds head `col`, tokens 4*grp + i of the tile
+  f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(b.k[s]), qv[s], sc, 0, 0, 0);
+  const bool full = valid >= 16;
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = full || (4 * grp + i < valid);
+    x[i] = ok ? sc[i] * p.scale_log2 : kNegInf;
+  }
+  const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__any(lmax > st.m_run + kLazyMax)) {
+    float mt = fmaxf(lmax, __shfl_xor(lmax, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(st.m_run, mt);
+    const float alpha = fast_exp2(st.m_run - m_new);  // 0 on the first tile
+    st.l_run *= alpha;
+    // rows of acc are heads 4*grp + r; their factor lives in lane 4*grp + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+      for (int nt = 0; nt < DV; ++nt) st.acc[nt][r] *= a;
+    }
+    st.m_run = m_new;
+  }
+  float pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - st.m_run);
+  st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+  if (!full) {  // zero V rows past the end (they may hold anything, NaN included)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * grp + j >= valid) b.v[j] = VRowT<D>{};
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&b.v[j]);
+#pragma unroll
+    for (int nt = 0; nt < DV; ++nt) {
+      const float v = (nt & 1) ? bf16_hi(w[nt >> 1]) : bf16_lo(w[nt >> 1]);
+      st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[j], v, st.acc[nt], 0, 0, 0);
+    }
+  }
+}
+
 // Tiles [tile_begin, tile_end) of segment (seq, kvh) whose context is n
-// tokens, accumulated into st.  The tiles may touch at most 64 blocks (one
-// block id per lane).
-//
-// The running max is moved only when a score exceeds it by more than
-// kLazyMax, so every weight 2^(x - m_run) stays <= 2^kLazyMax and the common
-// path needs no cross-lane traffic; results are exact either way (partials
-// carry m_run as their reference point).
+// tokens, accumulated into st (fixed-partition path).  The tiles may touch
+// at most 64 blocks (one block id per lane).  A ring of kRing tiles stays in
+// registers, kRing - 1 in flight while one is computed.
 template <int D, int BS>
 __device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int kvh, int n,
                                            int tile_begin, int tile_end,
                                            const bf16x8_t (&qv)[D / 32], MfmaState<D>& st,
                                            int lane) {
-  constexpr int KSTEPS = D / 32;  // QK k-steps
-  constexpr int DV = D / 16;      // V dims per lane per row == PV n-tiles
-  using VRow = typename std::conditional<DV == 8, uint4, uint2>::type;
-  struct Tile {
-    uint4 k[KSTEPS];  // key `col`, granule 4*s + grp (dims 32*s + 8*grp .. +7)
-    VRow v[4];        // value row 4*grp + j, dims DV*col .. +DV-1
-  };
+  constexpr int DV = D / 16;
   const int grp = lane >> 4;
   const int col = lane & 15;
   const int start = 16 * tile_begin;
@@ -171,25 +253,14 @@ __device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int k
     return ((int64_t)phys * p.num_kv_heads + kvh) * ((int64_t)BS * D);
   };
 
-  // Tile index clamped to the last tile: the ring is refilled
-  // unconditionally, and a refill past the end reads one 16-byte granule per
-  // instruction (all lanes the same address), never used.
-  auto load = [&](int t, Tile& b) {
+  auto load = [&](int t, Tile<D>& b) {
     const bool past = t >= ntiles;
     const int tb = start + 16 * min(t, ntiles - 1);
     if constexpr (BS >= 16) {
-      const int phys = __builtin_amdgcn_readlane(my_id, tb / BS - b0);
-      const int64_t cb = chunk_base(phys);
-      const int o = tb % BS;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        b.k[s] = load_stream(reinterpret_cast<const uint4*>(
-            kpool + cb + (past ? 0 : ((int64_t)(4 * s + grp) * BS + o + col) * 8)));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b.v[j] = load_stream(reinterpret_cast<const VRow*>(
-            vpool + cb + (past ? 0 : (int64_t)(o + 4 * grp + j) * D + DV * col)));
+      load_tile<D, BS>(kpool, vpool, chunk_base(__builtin_amdgcn_readlane(my_id, tb / BS - b0)),
+                       tb % BS, past, lane, b);
     } else {
+      // a tile spans two blocks: each lane fetches its row's id with a shuffle
       auto blk_base = [&](int tok) -> int64_t {
         const int lb = min(tok / BS - b0, nblk - 1);
         return chunk_base(__shfl(my_id, lb));
@@ -197,65 +268,14 @@ __device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int k
       const int kt = tb + col;
       const int64_t kb = blk_base(kt);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
+      for (int s = 0; s < D / 32; ++s)
         b.k[s] = load_stream(reinterpret_cast<const uint4*>(
             kpool + kb + (past ? 0 : ((int64_t)(4 * s + grp) * BS + kt % BS) * 8)));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int vt = tb + 4 * grp + j;
-        b.v[j] = load_stream(reinterpret_cast<const VRow*>(
+        b.v[j] = load_stream(reinterpret_cast<const VRowT<D>*>(
             vpool + blk_base(vt) + (past ? 0 : (int64_t)(vt % BS) * D + DV * col)));
-      }
-    }
-  };
-
-  auto compute = [&](int t, Tile& b) {
-    const int tb = start + 16 * t;
-    // scores: lane holds head `col`, tokens tb + 4*grp + i
-    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(b.k[s]), qv[s], sc, 0, 0, 0);
-    const bool full = tb + 16 <= end;
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = full || (tb + 4 * grp + i < end);
-      x[i] = ok ? sc[i] * p.scale_log2 : kNegInf;
-    }
-    const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    if (__any(lmax > st.m_run + kLazyMax)) {
-      float mt = fmaxf(lmax, __shfl_xor(lmax, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(st.m_run, mt);
-      const float alpha = fast_exp2(st.m_run - m_new);  // 0 on the first tile
-      st.l_run *= alpha;
-      // rows of acc are heads 4*grp + r; their factor lives in lane 4*grp + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float a = __shfl(alpha, 4 * grp + r);
-#pragma unroll
-        for (int nt = 0; nt < DV; ++nt) st.acc[nt][r] *= a;
-      }
-      st.m_run = m_new;
-    }
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - st.m_run);
-    st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-
-    if (!full) {  // zero V rows past the end (they may hold anything, NaN included)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (tb + 4 * grp + j >= end) b.v[j] = VRow{};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(&b.v[j]);
-#pragma unroll
-      for (int nt = 0; nt < DV; ++nt) {
-        const float v = (nt & 1) ? bf16_hi(w[nt >> 1]) : bf16_lo(w[nt >> 1]);
-        st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[j], v, st.acc[nt], 0, 0, 0);
       }
     }
   };
@@ -263,28 +283,16 @@ __device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int k
   // The first pass only fills the ring, so every path into a compute has
   // issued the ring's loads in the same order (the compiler can then wait for
   // the oldest tile alone).
-  Tile ring[kRing];
+  Tile<D> ring[kRing];
   for (int t0 = -kRing; t0 < ntiles; t0 += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       const int t = t0 + i;
-      if (t >= 0 && t < ntiles) compute(t, ring[i]);
+      if (t >= 0 && t < ntiles)
+        compute_tile<D>(p, st, qv, ring[i], min(16, end - (start + 16 * t)), lane);
       load(t + kRing, ring[i]);
     }
   }
-}
-
-// Tiles [tile_begin, tile_end) of a segment in calls of at most 64 blocks.
-template <int D, int BS>
-__device__ __forceinline__ void mfma_segment(const DecodeParams& p, int seq, int kvh, int n,
-                                             int tile_begin, int tile_end,
-                                             const bf16x8_t (&qv)[D / 32], MfmaState<D>& st,
-                                             int lane) {
-  // at most 64 blocks: a range of 63*BS tokens starting anywhere in a block
-  // (tiles start on 16-token boundaries; for BS == 8 they start on blocks)
-  constexpr int kMaxTiles = BS >= 16 ? (63 * BS) / 16 : 32;
-  for (int t = tile_begin; t < tile_end; t += kMaxTiles)
-    mfma_tiles<D, BS>(p, seq, kvh, n, t, min(t + kMaxTiles, tile_end), qv, st, lane);
 }
 
 // Write the G heads of a finished state: normalised into `out_row0` (head h
@@ -372,121 +380,245 @@ __device__ __forceinline__ int64_t streamk_workers(int64_t total_tiles, int laun
   return want < launched ? (want > 0 ? want : 1) : launched;
 }
 
+// Position of a tile in the (sequence, KV head, tile) order of all segments.
+struct Pos {
+  int seq, kvh, t;
+};
+
+// Move q forward by k tiles through the segments (sequences with an empty
+// context have no tiles and are stepped over); seq == S past the end.
+__device__ __forceinline__ Pos advance(Pos q, int k, const int* s_prefix, int S, int Hkv) {
+  q.t += k;
+  while (q.seq < S) {
+    const int nt = s_prefix[q.seq + 1] - s_prefix[q.seq];
+    if (q.t < nt) break;
+    q.t -= nt;
+    if (++q.kvh == Hkv) {
+      q.kvh = 0;
+      ++q.seq;
+    }
+  }
+  return q;
+}
+
+// Per-lane descriptors of up to 64 consecutive tiles, one per lane: the
+// tile's sequence, KV head and tile index, and the raw block-table entry of
+// its first token and context length of its sequence.  The two loads are
+// issued one chunk ahead of their use and only read (and checked) when the
+// tile's loads are issued, so building a chunk never waits for memory.
+struct TileDescs {
+  int seq, kvh, t, phys_raw, n_raw;
+  // Make the values register-resident at this point of the program, so the
+  // per-tile reads of a chunk never wait for memory where control flow joins.
+  __device__ __forceinline__ void settle() {
+    asm volatile("" : "+v"(seq), "+v"(kvh), "+v"(t), "+v"(phys_raw), "+v"(n_raw));
+  }
+};
+
+template <int BS>
+__device__ __forceinline__ TileDescs describe_tiles(const DecodeParams& p, const int* s_prefix,
+                                                    Pos start, int count, int lane) {
+  TileDescs d{0, 0, 0, 0, 0};
+  if (lane < count) {
+    const Pos q = advance(start, lane, s_prefix, p.num_seqs, p.num_kv_heads);
+    d.seq = q.seq;
+    d.kvh = q.kvh;
+    d.t = q.t;
+    d.n_raw = p.context_lens[q.seq];
+    d.phys_raw = p.block_tables[(int64_t)q.seq * p.max_blocks_per_seq + (16 * q.t) / BS];
+  }
+  return d;
+}
+
 template <int D, int BS>
 __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_kernel(
     const DecodeParams p) {
+  static_assert(BS >= 16, "stream-K tiles lie in one block");
   extern __shared__ int s_prefix[];  // [S+1]
   tile_prefix(p, s_prefix);
   const int S = p.num_seqs;
   const int Hkv = p.num_kv_heads;
+  const int G = p.group;
   const int64_t T = (int64_t)Hkv * s_prefix[S];
   const int64_t W = streamk_workers(T, p.max_workers);
-  if (blockIdx.x == 0) {  // publish the decomposition for the merge kernel
-    for (int i = threadIdx.x; i <= S; i += blockDim.x) p.ws_prefix[i] = s_prefix[i];
-    if (threadIdx.x == 0) {
-      p.ws_header[0] = T;
-      p.ws_header[1] = W;
-    }
-  }
   const int lane = threadIdx.x % kWave;
   const int64_t w = (int64_t)blockIdx.x * kDecodeWaves + wave_id();
-  if (T == 0 || w >= W) return;
+  int2* handoff = reinterpret_cast<int2*>(p.ws_handoff) + w;
+  if (T == 0 || w >= W) {
+    if (lane == 0) *handoff = make_int2(-1, -1);
+    return;
+  }
   const int64_t g0 = w * T / W;
   const int64_t g1 = (w + 1) * T / W;
-  const int G = p.group;
+  const int ntiles = (int)(g1 - g0);
 
-  // segment holding tile g0: the last sequence whose first tile is <= g0
-  int lo = 0, hi = S - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if ((int64_t)Hkv * s_prefix[mid] <= g0) lo = mid; else hi = mid - 1;
+  // position of tile g0: the last sequence whose first tile is <= g0
+  Pos pos0;
+  {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if ((int64_t)Hkv * s_prefix[mid] <= g0) lo = mid; else hi = mid - 1;
+    }
+    const int nt = s_prefix[lo + 1] - s_prefix[lo];
+    const int64_t off = g0 - (int64_t)Hkv * s_prefix[lo];
+    pos0.seq = lo;
+    pos0.kvh = (int)(off / nt);
+    pos0.t = (int)(off - (int64_t)pos0.kvh * nt);
   }
-  int seq = lo;
-  int nt = s_prefix[seq + 1] - s_prefix[seq];
-  int64_t seq0 = (int64_t)Hkv * s_prefix[seq];
-  int kvh = (int)((g0 - seq0) / nt);
-  int tb = (int)((g0 - seq0) - (int64_t)kvh * nt);
-  int64_t g = g0;
 
-  const int64_t slot0 = w * 2;
+  // descriptors: `dc` covers the chunk the loads are in, `dn` the next one
+  auto chunk_count = [&](int c) { return min(kWave, ntiles - c * kWave); };
+  TileDescs dc = describe_tiles<BS>(p, s_prefix, pos0, chunk_count(0), lane);
+  dc.settle();
+  Pos next_pos = advance(pos0, kWave, s_prefix, S, Hkv);
+  TileDescs dn = {0, 0, 0, 0, 0};
+  if (ntiles > kWave) {
+    dn = describe_tiles<BS>(p, s_prefix, next_pos, chunk_count(1), lane);
+    next_pos = advance(next_pos, kWave, s_prefix, S, Hkv);
+  }
+  int chunk = 0;
+
+  const uint16_t* kpool = static_cast<const uint16_t*>(p.k_cache);
+  const uint16_t* vpool = static_cast<const uint16_t*>(p.v_cache);
+
+  // compute-side state: the piece being accumulated
   MfmaState<D> st;
+  st.reset();
   bf16x8_t qv[D / 32];
-  while (g < g1) {
-    const int64_t seg_start = seq0 + (int64_t)kvh * nt;
-    const int te = (int)min<int64_t>(nt, g1 - seg_start);
-    const int n = clamp_ctx(p, seq);
+  int cur_seg = -1, cur_t0 = 0, cur_tlast = 0;
+  int2 my_handoff = make_int2(-1, -1);
+  const int64_t slot0 = w * 2;
+
+  auto finish_piece = [&]() {
+    const int seq = cur_seg / Hkv, kvh = cur_seg - (cur_seg / Hkv) * Hkv;
+    const int nt = s_prefix[seq + 1] - s_prefix[seq];
     const int hq0 = kvh * G;
-    mfma_load_q<D>(p, seq, hq0, lane, qv);
-    st.reset();
-    mfma_segment<D, BS>(p, seq, kvh, n, tb, te, qv, st, lane);
-    if (tb == 0 && te == nt) {
+    if (cur_t0 == 0 && cur_tlast == nt - 1) {
       mfma_finish<D>(st, G, lane, p.out + ((int64_t)seq * p.num_q_heads + hq0) * D, nullptr,
                      nullptr, nullptr, 0, 0);
     } else {
-      // slot 0: a segment begun by an earlier wave; slot 1: one continued by a later wave
-      const int64_t slot = slot0 + (tb > 0 ? 0 : 1);
+      // slot 0: a segment begun by an earlier wave; slot 1: one continued by
+      // later waves -- this wave is its first, so it hands the merge on
+      const int64_t slot = slot0 + (cur_t0 > 0 ? 0 : 1);
       mfma_finish<D>(st, G, lane, nullptr, p.ws_acc + slot * G * D, p.ws_m + slot * G,
                      p.ws_l + slot * G, D, 1);
+      if (cur_t0 == 0) {
+        const int64_t last_tile = (int64_t)Hkv * s_prefix[seq] + (int64_t)kvh * nt + nt - 1;
+        my_handoff = make_int2(cur_seg, (int)(((last_tile + 1) * W - 1) / T));
+      }
     }
-    g += te - tb;
-    tb = 0;
-    if (++kvh == Hkv) {
-      kvh = 0;
-      do {
-        ++seq;
-      } while (seq < S && s_prefix[seq + 1] == s_prefix[seq]);
-      if (seq >= S) break;
-      nt = s_prefix[seq + 1] - s_prefix[seq];
-      seq0 = (int64_t)Hkv * s_prefix[seq];
+  };
+
+  Tile<D> ring[kRing];
+  int ring_seg[kRing];
+  int ring_tv[kRing];
+
+  auto load = [&](int u, int i) {
+    const bool past = u >= ntiles;
+    const int uu = min(u, ntiles - 1);
+    if (uu / kWave != chunk) {  // entering the next chunk (its loads were issued a chunk ago)
+      chunk = uu / kWave;
+      dc = dn;  // loaded a chunk ago
+      dc.settle();
+      if ((chunk + 1) * kWave < ntiles) {
+        dn = describe_tiles<BS>(p, s_prefix, next_pos, chunk_count(chunk + 1), lane);
+        next_pos = advance(next_pos, kWave, s_prefix, S, Hkv);
+      }
+    }
+    const int l = uu % kWave;
+    const int seq = __builtin_amdgcn_readlane(dc.seq, l);
+    const int kvh = __builtin_amdgcn_readlane(dc.kvh, l);
+    const int t = __builtin_amdgcn_readlane(dc.t, l);
+    int phys = __builtin_amdgcn_readlane(dc.phys_raw, l);
+    phys = (phys >= 0 && phys < p.num_blocks) ? phys : 0;  // a bad entry reads block 0
+    const int n = min(max(__builtin_amdgcn_readlane(dc.n_raw, l), 0), p.max_tokens);
+    const int seg = seq * Hkv + kvh;
+    const int tv = (t << 5) | min(16, n - 16 * t);
+    const int64_t cb = ((int64_t)phys * Hkv + kvh) * ((int64_t)BS * D);
+    load_tile<D, BS>(kpool, vpool, cb, (16 * (tv >> 5)) % BS, past, lane, ring[i]);
+    ring_seg[i] = past ? -1 : seg;
+    ring_tv[i] = tv;
+  };
+
+  auto compute = [&](int i) {
+    const int seg = ring_seg[i];
+    const int tv = ring_tv[i];
+    if (seg != cur_seg) {
+      if (cur_seg >= 0) finish_piece();
+      // Q of the new segment is read here, while the ring's loads stay in
+      // flight.  (Staging it earlier in spare registers costs register
+      // copies at the loop's join points, and a copy of a register with a
+      // pending load waits for that load.)
+      const int kvh = seg - (seg / Hkv) * Hkv;
+      mfma_load_q<D>(p, seg / Hkv, kvh * G, lane, qv);
+      // Q must be in registers on this rarely taken path: otherwise the wait
+      // for it lands where the paths join and drains every tile's loads.
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) asm volatile("" : "+v"(qv[s]));
+      st.reset();
+      cur_seg = seg;
+      cur_t0 = tv >> 5;
+    }
+    compute_tile<D>(p, st, qv, ring[i], tv & 31, lane);
+    cur_tlast = tv >> 5;
+  };
+
+  // The first pass only fills the ring, so every path into a compute has
+  // issued the ring's loads in the same order.
+  for (int u0 = -kRing; u0 < ntiles; u0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int u = u0 + i;
+      if (u >= 0 && u < ntiles) compute(i);
+      load(u + kRing, i);
     }
   }
+  finish_piece();
+  if (lane == 0) *handoff = my_handoff;
 }
 
-// One workgroup per segment (sequence, KV head).  Segments split across
-// waves are merged from their partials: slot 1 of the first wave, slot 0 of
-// the others (in wave order); an empty segment gets zeros.
+// One workgroup per launched wave slot w.  If wave w handed a segment on, it
+// is merged here from slot 1 of wave w and slot 0 of waves w+1 .. last, in
+// wave order, with an online log-sum-exp rescale.  Every workgroup also
+// writes zeros for its share of the sequences with an empty context.
 template <int D>
 __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeParams p) {
   constexpr int C = D / 4;  // float4 chunks per row
-  const int e = blockIdx.x;
-  const int Hkv = p.num_kv_heads;
-  const int seq = e / Hkv, kvh = e % Hkv;
   const int G = p.group;
-  const int hq0 = kvh * G;
-  const int nt = p.ws_prefix[seq + 1] - p.ws_prefix[seq];
-  float* out = p.out + ((int64_t)seq * p.num_q_heads + hq0) * D;
-  if (nt == 0) {
-    for (int idx = threadIdx.x; idx < G * C; idx += blockDim.x)
-      reinterpret_cast<float4*>(out)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
+  for (int seq = blockIdx.x; seq < p.num_seqs; seq += gridDim.x) {
+    if (clamp_ctx(p, seq) > 0) continue;
+    float4* out = reinterpret_cast<float4*>(p.out + (int64_t)seq * p.num_q_heads * D);
+    for (int idx = threadIdx.x; idx < p.num_q_heads * C; idx += blockDim.x)
+      out[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const int64_t T = p.ws_header[0];
-  const int64_t W = p.ws_header[1];
-  const int64_t first = (int64_t)Hkv * p.ws_prefix[seq] + (int64_t)kvh * nt;
-  const int64_t w1 = ((first + 1) * W - 1) / T;           // wave owning the first tile
-  const int64_t w2 = ((first + nt) * W - 1) / T;          // wave owning the last tile
-  if (w1 == w2) return;                                    // written whole by one wave
+  const int64_t w1 = blockIdx.x;
+  const int2 h = reinterpret_cast<const int2*>(p.ws_handoff)[w1];
+  if (h.x < 0) return;
+  const int seq = h.x / p.num_kv_heads, kvh = h.x % p.num_kv_heads;
+  const int64_t w2 = h.y;
+  float* out = p.out + ((int64_t)seq * p.num_q_heads + kvh * G) * D;
   for (int idx = threadIdx.x; idx < G * C; idx += blockDim.x) {
-    const int h = idx / C, c = idx % C;
-    float M = kNegInf;
-    for (int64_t w = w1; w <= w2; ++w) {
-      const int64_t slot = 2 * w + (w == w1 ? 1 : 0);
-      M = fmaxf(M, p.ws_m[slot * G + h]);
-    }
-    float L = 0.f;
+    const int hd = idx / C, c = idx % C;
+    float M = kNegInf, L = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int64_t w = w1; w <= w2; ++w) {
       const int64_t slot = 2 * w + (w == w1 ? 1 : 0);
-      const float wt = fast_exp2(p.ws_m[slot * G + h] - M);
-      L = fmaf(wt, p.ws_l[slot * G + h], L);
-      const float4 v = reinterpret_cast<const float4*>(p.ws_acc + (slot * G + h) * D)[c];
-      a.x = fmaf(wt, v.x, a.x);
-      a.y = fmaf(wt, v.y, a.y);
-      a.z = fmaf(wt, v.z, a.z);
-      a.w = fmaf(wt, v.w, a.w);
+      const float m = p.ws_m[slot * G + hd];
+      const float l = p.ws_l[slot * G + hd];
+      const float4 v = reinterpret_cast<const float4*>(p.ws_acc + (slot * G + hd) * D)[c];
+      const float Mn = fmaxf(M, m);
+      const float s_old = fast_exp2(M - Mn);   // 0 while M is -inf
+      const float s_new = fast_exp2(m - Mn);
+      L = L * s_old + l * s_new;
+      a.x = a.x * s_old + v.x * s_new;
+      a.y = a.y * s_old + v.y * s_new;
+      a.z = a.z * s_old + v.z * s_new;
+      a.w = a.w * s_old + v.w * s_new;
+      M = Mn;
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    reinterpret_cast<float4*>(out + (int64_t)h * D)[c] =
+    reinterpret_cast<float4*>(out + (int64_t)hd * D)[c] =
         make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
   }
 }
@@ -758,15 +890,14 @@ hipError_t launch_streamk(const DecodeParams& p, hipStream_t stream) {
                      dim3(kDecodeWaves * kWave), lds, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_streamk_merge_kernel<D>), dim3(p.num_seqs * p.num_kv_heads),
-                     dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((decode_streamk_merge_kernel<D>), dim3(blocks * kDecodeWaves), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_streamk_bs(const DecodeParams& p, int block_size, hipStream_t stream) {
   switch (block_size) {
-    case 8: return launch_streamk<D, 8>(p, stream);
     case 16: return launch_streamk<D, 16>(p, stream);
     case 32: return launch_streamk<D, 32>(p, stream);
     default: return launch_streamk<D, 64>(p, stream);
@@ -821,8 +952,10 @@ int streamk_workers_per_cu(int head_dim) {
   return blocks * kDecodeWaves;
 }
 
-DecodePath decode_path(int num_seqs, pa_dtype dtype, int partition_size, bool vector_only) {
-  if (dtype == PA_BF16 && !vector_only && partition_size == 0 && num_seqs <= kStreamKMaxSeqs)
+DecodePath decode_path(int num_seqs, int block_size, pa_dtype dtype, int partition_size,
+                       bool vector_only) {
+  if (dtype == PA_BF16 && !vector_only && partition_size == 0 && num_seqs <= kStreamKMaxSeqs &&
+      block_size >= 16)
     return DecodePath::kStreamK;
   return DecodePath::kPartition;
 }
@@ -840,11 +973,11 @@ DecodeWorkspace decode_workspace_partition(int num_seqs, int num_q_heads, int he
 }
 
 DecodeWorkspace decode_workspace_streamk(int num_seqs, int group, int head_dim) {
+  (void)num_seqs;
   DecodeWorkspace w{};
   const size_t slots = (size_t)kStreamKMaxWorkers * 2 * group;
-  w.header_off = 0;
-  w.prefix_off = 256;
-  w.m_off = w.prefix_off + align256((size_t)(num_seqs + 1) * sizeof(int));
+  w.handoff_off = 0;
+  w.m_off = align256((size_t)kStreamKMaxWorkers * 2 * sizeof(int32_t));
   w.l_off = w.m_off + align256(slots * sizeof(float));
   w.acc_off = w.l_off + align256(slots * sizeof(float));
   w.total = w.acc_off + align256(slots * head_dim * sizeof(float));

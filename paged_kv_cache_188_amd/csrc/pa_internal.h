@@ -38,8 +38,8 @@ struct DecodeParams {
   float* ws_m;        // running maxima (log2 domain; the reference point of l and acc)
   float* ws_l;        // running sums
   float* ws_acc;      // unnormalised outputs
-  int32_t* ws_prefix; // stream-K: [S+1] tile prefix over sequences, written by the decode kernel
-  int64_t* ws_header; // stream-K: {total tiles T, workers W}, written by the decode kernel
+  int32_t* ws_handoff; // stream-K: [max_workers][2] per wave {segment it hands on, last wave
+                       // sharing it} or {-1, -1}; every launched wave writes its entry
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
@@ -64,14 +64,15 @@ enum class DecodePath { kStreamK, kPartition };
 int streamk_workers_per_cu(int head_dim);
 
 // Which path pa_decode_attention takes (host rule shared with the size query).
-DecodePath decode_path(int num_seqs, pa_dtype dtype, int partition_size, bool vector_only);
+DecodePath decode_path(int num_seqs, int block_size, pa_dtype dtype, int partition_size,
+                       bool vector_only);
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, pa_dtype dtype,
                          bool vector_only, DecodePath path, hipStream_t stream);
 
 // Workspace offsets (bytes); shared by the size query and the launch.
 struct DecodeWorkspace {
-  size_t m_off, l_off, acc_off, prefix_off, header_off, total;
+  size_t m_off, l_off, acc_off, handoff_off, total;
 };
 DecodeWorkspace decode_workspace_partition(int num_seqs, int num_q_heads, int head_dim,
                                            int max_partitions);

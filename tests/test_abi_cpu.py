@@ -117,10 +117,11 @@ def test_workspace_and_partition_rules(lib):
     assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072, 512) == al(rows * 4) * 2 + al(rows * d * 4)
     assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072, 0, dtype=f32) == \
         pa.decode_workspace_size(s, hq, 8, d, 32, 131072, 1024)
-    # stream-K (bf16, library choice): header, prefix, then 2048 waves x 2 slots x G heads
+    # stream-K (bf16, library choice): a hand-off entry per wave, then 2048 waves x 2
+    # slots x G heads of (m, l, acc)
     g = 8
     slots = 2048 * 2 * g
-    want = 256 + al((s + 1) * 4) + 2 * al(slots * 4) + al(slots * d * 4)
+    want = al(2048 * 8) + 2 * al(slots * 4) + al(slots * d * 4)
     assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072) == want
     assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072, vector_only=True) == \
         pa.decode_workspace_size(s, hq, 8, d, 32, 131072, dtype=f32)

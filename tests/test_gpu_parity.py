@@ -123,6 +123,40 @@ def test_edge_shapes(shape):
         assert np.isfinite(out).all()
 
 
+# Work splits of the stream-K path (bf16, block size >= 16): many segments
+# per wave (segment switches inside a wave's pipeline), contexts of one tile,
+# empty contexts between non-empty ones, and one context split over ~150
+# waves whose partials are merged.
+def _mixed_ctx(rng, n):
+    c = rng.integers(1, 49, size=n)
+    c[rng.random(n) < 0.2] = 0
+    return c
+
+
+STREAMK_CASES = [
+    # name, ctx recipe, Hq, Hkv, D, bs
+    ("many-short", lambda r: _mixed_ctx(r, 3000), 8, 2, 128, 16),
+    ("many-short-g16-d64", lambda r: _mixed_ctx(r, 1500), 16, 1, 64, 64),
+    ("one-long", lambda r: [20000], 4, 1, 128, 32),
+    ("long-and-empty", lambda r: [0, 9000, 0, 0, 1, 17, 5000, 0], 16, 4, 128, 16),
+]
+
+
+@pytest.mark.parametrize("case", STREAMK_CASES, ids=lambda c: c[0])
+def test_streamk_splits(case):
+    name, recipe, hq, hkv, d, bs = case
+    rng = np.random.default_rng(sum(map(ord, name)))
+    ctx = np.asarray(recipe(rng), dtype=np.int32)
+    wl = W.decode_workload(f"streamk {name}", "bf16", ctx, hq, hkv, d, bs, rng=rng,
+                           seed=(11, len(ctx), hq, hkv, d, bs))
+    out, ref = run_both(wl, check_pools=False)
+    err = max_abs_err(out, ref)
+    _say(f"  max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.all(out[ctx == 0] == 0.0)
+    assert np.isfinite(out).all()
+
+
 def test_single_token_is_exact_value_row():
     """ctx == 1: the output equals the only V row (exact in float32)."""
     rng = np.random.default_rng(3)
