@@ -51,8 +51,9 @@ def parse():
 
 
 def cpu_baseline(wl, budget_s):
-    """The oracle, as it stands, on the first sequences of the same workload
-    until `budget_s` seconds have passed (at least one sequence)."""
+    """The oracle, as it stands, on the sequences of the same workload in
+    order (starting over after the last) until `budget_s` seconds have passed
+    (at least one sequence)."""
     import resource
 
     import numpy as np
@@ -71,22 +72,43 @@ def cpu_baseline(wl, budget_s):
     kv = 0
     r0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
-    while done < wl.num_seqs and (done == 0 or time.perf_counter() - t0 < budget_s):
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        i = done % wl.num_seqs
         O.decode_attention(wl.q, kp, vp, wl.tables["final"], wl.context_lens, wl.scale, wl.dtype,
-                           seqs=[done])
-        kv += int(wl.context_lens[done]) * wl.num_kv_heads * wl.head_dim * 2 * (2 if wl.dtype == "bf16" else 4)
+                           seqs=[i])
+        kv += int(wl.context_lens[i]) * wl.num_kv_heads * wl.head_dim * 2 * (2 if wl.dtype == "bf16" else 4)
         done += 1
     wall = time.perf_counter() - t0
     r1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
     return {
         "value": kv / wall / 1e9, "unit": "GB/s", "cores": round(cpu / wall, 2), "kind": "oracle",
-        "sample": (f"float64 numpy oracle decode of the first {done} of {wl.num_seqs} sequences "
-                   f"(all {wl.num_q_heads} query heads) of the same workload: {wall:.1f} s wall, "
+        "sample": (f"float64 numpy oracle decode, one sequence (all {wl.num_q_heads} query heads) "
+                   f"per call, {done} sequence-steps cycling over the {wl.num_seqs} sequences of "
+                   f"the same workload ({done / wl.num_seqs:.2f} passes): {wall:.1f} s wall, "
                    f"{done / wall:.2f} seq-steps/s; cores = CPU time / wall time; "
                    f"BLAS pool {blas} threads; host affinity {len(os.sched_getaffinity(0))} cpus"),
         "seq_steps_per_s": done / wall,
     }
+
+
+def measured_traffic(wl):
+    """HBM bytes per decode call from the committed counter summary, if it was
+    taken on this workload with the decode source as it is now (else None)."""
+    import hashlib
+    src = os.path.join(ROOT, "paged_kv_cache_188_amd", "csrc", "pa_decode.hip")
+    path = os.path.join(ROOT, "profiles", "decode_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != sha or kv.get("workload") != wl.name:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def calibrate_copy(steps):
@@ -165,6 +187,16 @@ def main():
     wall = time.perf_counter() - t0
 
     ms_step = wall * 1e3 / args.steps
+    workers = pa.decode_streamk_workers(wl.num_seqs, wl.head_dim, wl.block_size,
+                                        wl.partition_size, dev.torch_dtype)
+    if workers > 0:
+        decomposition = {"path": "stream-K", "persistent_waves": workers}
+        kernel = ("pa_decode_attention: decode_mfma_streamk_kernel + decode_streamk_merge_kernel "
+                  "(events around the call)")
+    else:
+        decomposition = {"path": "fixed partitions", "partition_size": pa.decode_partition_size(
+            wl.num_seqs, wl.num_kv_heads, wl.block_size, wl.max_context_len, wl.partition_size)}
+        kernel = "pa_decode_attention: decode_mfma_kernel + decode_reduce_kernel (events around the call)"
     dec_ms = [a.elapsed_time(b) for a, b in events]
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     kv_bytes = wl.kv_bytes_read()
@@ -191,9 +223,7 @@ def main():
             "block_size": wl.block_size, "num_blocks": wl.num_blocks,
             "sum_context_tokens": int(wl.context_lens.sum()),
             "max_context_len": wl.max_context_len,
-            "partition_size": pa.decode_partition_size(wl.num_seqs, wl.num_kv_heads,
-                                                       wl.block_size, wl.max_context_len,
-                                                       wl.partition_size),
+            "decomposition": decomposition,
             "seed": list(wl.seed), "pool_copies_rotated": npools,
             "parallelism": "single GPU",
         },
@@ -203,11 +233,12 @@ def main():
         "decode_ms": {"avg": round(dec_avg_ms, 5), "min": round(min(dec_ms), 5),
                       "max": round(max(dec_ms), 5)},
         "roofline": {
-            "kernel": "pa_decode_attention (decode kernel + partition merge)",
+            "kernel": kernel,
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl),
             "algorithmic_bytes_per_launch": dec_bytes,
+            "avg_launch_us": round(dec_avg_ms * 1e3, 2),
         },
     }
     if not args.no_cpu_baseline:

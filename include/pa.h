@@ -175,8 +175,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
  * sizes the fixed-partition grid and workspace (a larger bound is correct,
  * just slower).
  *
- * Work decomposition.  With partition_size == 0, bf16 K/V, flags == 0 and
- * num_seqs <= 8192 the library splits the (sequence, KV head, 16-token tile)
+ * Work decomposition.  With partition_size == 0, bf16 K/V, flags == 0,
+ * block_size >= 16 and num_seqs <= 8192 the library splits the (sequence, KV head, 16-token tile)
  * work evenly over one wave per resident wave slot of the device
  * ("stream-K"); a context shared by two waves is merged from float32
  * partials with an exact log-sum-exp rescale.  Otherwise each context is cut
@@ -198,6 +198,14 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
                                  int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size);
+
+/* Waves the stream-K path launches for these arguments on the current
+ * device (one per resident wave slot, at most 2048), 0 when the call takes
+ * the fixed-partition path, -1 for unsupported arguments or a HIP error.
+ * Only the fixed-partition answer is available without a GPU.               */
+int32_t pa_decode_streamk_workers(int32_t num_seqs, int32_t head_dim,
+                                  int32_t block_size, int32_t partition_size,
+                                  pa_dtype dtype, uint32_t flags);
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim,

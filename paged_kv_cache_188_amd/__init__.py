@@ -39,6 +39,7 @@ SIGNATURES = {
                                    ctypes.c_int, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
     "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_streamk_workers": (_I32, [_I32, _I32, _I32, _I32, ctypes.c_int, ctypes.c_uint32]),
     "pa_decode_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                     ctypes.c_int, ctypes.c_uint32]),
     "pa_decode_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
@@ -179,6 +180,15 @@ def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
 def decode_partition_size(num_seqs, num_kv_heads, block_size, max_context_len, partition_size=0):
     return int(lib().pa_decode_partition_size(num_seqs, num_kv_heads, block_size,
                                               max_context_len, partition_size))
+
+
+def decode_streamk_workers(num_seqs, head_dim, block_size, partition_size=0, dtype=None,
+                           vector_only=False):
+    """Waves the stream-K path launches (0: the call takes fixed partitions)."""
+    import torch
+    code = PA_F32 if dtype == torch.float32 else PA_BF16
+    return int(lib().pa_decode_streamk_workers(num_seqs, head_dim, block_size, partition_size,
+                                               code, PA_DECODE_VECTOR_ONLY if vector_only else 0))
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,

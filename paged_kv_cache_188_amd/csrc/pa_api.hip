@@ -150,6 +150,20 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t
   return choose_partition(num_seqs, num_kv_heads, block_size, max_context_len);
 }
 
+int32_t pa_decode_streamk_workers(int32_t num_seqs, int32_t head_dim, int32_t block_size,
+                                  int32_t partition_size, pa_dtype dtype, uint32_t flags) {
+  if (num_seqs < 0 || !supported_head_dim(head_dim) || !supported_block_size(block_size) ||
+      !valid_dtype(dtype) || (flags & ~PA_DECODE_VECTOR_ONLY))
+    return -1;
+  const bool vector_only = (flags & PA_DECODE_VECTOR_ONLY) != 0;
+  if (pa::decode_path(num_seqs, block_size, dtype, partition_size, vector_only) !=
+      pa::DecodePath::kStreamK)
+    return 0;
+  int workers = 0;
+  if (streamk_workers(head_dim, &workers) != 0) return -1;
+  return workers;
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                 int32_t partition_size, pa_dtype dtype, uint32_t flags) {

@@ -602,20 +602,33 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
     const int hd = idx / C, c = idx % C;
     float M = kNegInf, L = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t w = w1; w <= w2; ++w) {
-      const int64_t slot = 2 * w + (w == w1 ? 1 : 0);
-      const float m = p.ws_m[slot * G + hd];
-      const float l = p.ws_l[slot * G + hd];
-      const float4 v = reinterpret_cast<const float4*>(p.ws_acc + (slot * G + hd) * D)[c];
-      const float Mn = fmaxf(M, m);
-      const float s_old = fast_exp2(M - Mn);   // 0 while M is -inf
-      const float s_new = fast_exp2(m - Mn);
-      L = L * s_old + l * s_new;
-      a.x = a.x * s_old + v.x * s_new;
-      a.y = a.y * s_old + v.y * s_new;
-      a.z = a.z * s_old + v.z * s_new;
-      a.w = a.w * s_old + v.w * s_new;
-      M = Mn;
+    // four partials per round trip: all loads of a batch are issued first
+    // (indices past w2 re-read w2's and are not combined)
+    constexpr int kBatch = 4;
+    for (int64_t wb = w1; wb <= w2; wb += kBatch) {
+      float m[kBatch], l[kBatch];
+      float4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t w = wb + u <= w2 ? wb + u : w2;
+        const int64_t slot = 2 * w + (w == w1 ? 1 : 0);
+        m[u] = p.ws_m[slot * G + hd];
+        l[u] = p.ws_l[slot * G + hd];
+        v[u] = reinterpret_cast<const float4*>(p.ws_acc + (slot * G + hd) * D)[c];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (wb + u > w2) break;
+        const float Mn = fmaxf(M, m[u]);
+        const float s_old = fast_exp2(M - Mn);   // 0 while M is -inf
+        const float s_new = fast_exp2(m[u] - Mn);
+        L = L * s_old + l[u] * s_new;
+        a.x = a.x * s_old + v[u].x * s_new;
+        a.y = a.y * s_old + v[u].y * s_new;
+        a.z = a.z * s_old + v[u].z * s_new;
+        a.w = a.w * s_old + v[u].w * s_new;
+        M = Mn;
+      }
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     reinterpret_cast<float4*>(out + (int64_t)hd * D)[c] =

@@ -223,6 +223,33 @@ def test_run_to_run_determinism():
     assert a.tobytes() == b.tobytes() == c.tobytes()
 
 
+def test_workspace_reuse_with_new_queries():
+    """Consecutive calls on one workspace: partials and arrival counters left
+    by a call never leak into the next (new queries give the oracle's new
+    answer; the old queries give the old answer again, bit for bit)."""
+    import copy
+    from workloads.device import to_device
+    for cid in (2, 3):
+        wl = W.make(cid, small=True)
+        DeviceWorkload = _device()
+        dev = DeviceWorkload(wl)
+        dev.run_setup()
+        a = dev.run_step().cpu().numpy()
+        w2 = copy.copy(wl)
+        w2.q = W.draw_normal(np.random.default_rng(99 + cid), wl.q.shape, wl.dtype)
+        q_old = dev.q
+        dev.q = to_device(w2.q, wl.dtype)
+        b = dev.decode_only().cpu().numpy()
+        dev.q = q_old
+        c = dev.decode_only().cpu().numpy()
+        torch.cuda.synchronize()
+        _, _, ref_b, _ = run_oracle(w2, w2.setup + w2.step)
+        err = max_abs_err(b, ref_b)
+        _say(f"  config {cid}: new-query max_abs_err={err:.3e}")
+        assert err <= TOL[wl.dtype]
+        assert a.tobytes() == c.tobytes()
+
+
 def test_shared_prefix_equals_private_copies():
     """Invariant (b): samples that share physical prefix blocks get, bit for
     bit, the outputs they get when every sample owns a private copy."""
