@@ -41,12 +41,14 @@
 //   softmax: online (running max m, running sum l) per head, base 2 with the
 //          scale folded in; masked tokens get -inf by select, never by
 //          multiplication, so NaN in unused slots cannot leak.
-//   PV   : v_mfma_f32_16x16x4_f32, A = P (16 heads x 4 tokens, full float32),
-//          B = V (4 tokens x 16 dims).  The token order inside a k-step is
-//          free, so step j uses lane (grp, col)'s own score register j (token
-//          4*grp + j) and its own V load: row 4*grp + j, dims (D/16)*col ..
-//          +D/16-1 of the token-major V pool (16 lanes read one V row).
-//          Output: lane holds heads 4*grp + r, dims (D/16)*col + nt.
+//   PV   : v_mfma_f32_16x16x16_bf16 twice per output tile, A = P split as
+//          hi + lo bf16 (16 heads x 16 tokens; hi + lo equals the float32
+//          weight to 2^-16 relative, so P is never rounded to bf16), B = V
+//          (16 tokens x 16 dims).  Lane (grp, col) holds the scores of tokens
+//          4*grp .. 4*grp+3 (the A layout) and loads V rows 4*grp + j, dims
+//          (D/16)*col .. +D/16-1 of the token-major V pool (16 lanes read one
+//          V row); element nt of its four rows is the B operand of output
+//          tile nt.  Output: lane holds heads 4*grp + r, dims (D/16)*col + nt.
 //   pipeline: a ring of 4 tiles in registers, 3 in flight while one is
 //          computed.
 //
@@ -66,6 +68,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));   // 4 bf16 bit patterns
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kDecodeWaves = 4;  // independent waves per workgroup
 constexpr int kRing = 4;         // 16-token tiles held in registers per wave (3 in flight)
@@ -210,14 +215,39 @@ __device__ __forceinline__ void compute_tile(const DecodeParams& p, MfmaState<D>
     for (int j = 0; j < 4; ++j)
       if (4 * grp + j >= valid) b.v[j] = VRowT<D>{};
   }
+  // PV on the bf16 matrix cores without rounding P to bf16: p = hi + lo with
+  // hi = the upper 16 bits of p (exact) and lo = bf16(p - hi) (p - hi is
+  // exact in float32), so hi + lo equals p to 2^-16 relative; bf16 x bf16
+  // products are exact and accumulate in float32.  A operand: lane (grp,
+  // col) holds head col, tokens 4*grp .. 4*grp+3 -- the scores' own layout.
+  uint32_t u[4];
+  float r[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(&b.v[j]);
+  for (int i = 0; i < 4; ++i) {
+    u[i] = __float_as_uint(pr[i]);
+    r[i] = pr[i] - __uint_as_float(u[i] & 0xffff0000u);
+  }
+  const s16x4_t p_hi = __builtin_bit_cast(
+      s16x4_t, make_uint2(__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
+                          __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)));
+  const s16x4_t p_lo = __builtin_bit_cast(
+      s16x4_t,
+      make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[0], r[1]}, bf16x2_t)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[2], r[3]}, bf16x2_t))));
+  // B operand of output tile nt: tokens 4*grp .. 4*grp+3 of dim (D/16)*col +
+  // nt, i.e. element nt of this lane's four V rows, packed pairwise.
+  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&b.v[0]);
+  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&b.v[1]);
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&b.v[2]);
+  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&b.v[3]);
 #pragma unroll
-    for (int nt = 0; nt < DV; ++nt) {
-      const float v = (nt & 1) ? bf16_hi(w[nt >> 1]) : bf16_lo(w[nt >> 1]);
-      st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[j], v, st.acc[nt], 0, 0, 0);
-    }
+  for (int nt = 0; nt < DV; ++nt) {
+    const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+    const s16x4_t v = __builtin_bit_cast(
+        s16x4_t, make_uint2(__builtin_amdgcn_perm(w1[nt >> 1], w0[nt >> 1], sel),
+                            __builtin_amdgcn_perm(w3[nt >> 1], w2[nt >> 1], sel)));
+    st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, v, st.acc[nt], 0, 0, 0);
+    st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, v, st.acc[nt], 0, 0, 0);
   }
 }
 
