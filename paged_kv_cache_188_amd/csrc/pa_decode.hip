@@ -469,6 +469,13 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
   const int S = p.num_seqs;
   const int Hkv = p.num_kv_heads;
   const int G = p.group;
+  // sequences with an empty context: zeros, spread over the workgroups
+  for (int seq = blockIdx.x; seq < S; seq += gridDim.x) {
+    if (s_prefix[seq + 1] != s_prefix[seq]) continue;
+    float4* o = reinterpret_cast<float4*>(p.out + (int64_t)seq * p.num_q_heads * D);
+    for (int i = threadIdx.x; i < p.num_q_heads * (D / 4); i += blockDim.x)
+      o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int64_t T = (int64_t)Hkv * s_prefix[S];
   const int64_t W = streamk_workers(T, p.max_workers);
   const int lane = threadIdx.x % kWave;
@@ -610,18 +617,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
 
 // One workgroup per launched wave slot w.  If wave w handed a segment on, it
 // is merged here from slot 1 of wave w and slot 0 of waves w+1 .. last, in
-// wave order, with an online log-sum-exp rescale.  Every workgroup also
-// writes zeros for its share of the sequences with an empty context.
+// wave order, with an online log-sum-exp rescale.
 template <int D>
 __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeParams p) {
   constexpr int C = D / 4;  // float4 chunks per row
   const int G = p.group;
-  for (int seq = blockIdx.x; seq < p.num_seqs; seq += gridDim.x) {
-    if (clamp_ctx(p, seq) > 0) continue;
-    float4* out = reinterpret_cast<float4*>(p.out + (int64_t)seq * p.num_q_heads * D);
-    for (int idx = threadIdx.x; idx < p.num_q_heads * C; idx += blockDim.x)
-      out[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   const int64_t w1 = blockIdx.x;
   const int2 h = reinterpret_cast<const int2*>(p.ws_handoff)[w1];
   if (h.x < 0) return;
@@ -632,9 +632,9 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
     const int hd = idx / C, c = idx % C;
     float M = kNegInf, L = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    // four partials per round trip: all loads of a batch are issued first
+    // eight partials per round trip: all loads of a batch are issued first
     // (indices past w2 re-read w2's and are not combined)
-    constexpr int kBatch = 4;
+    constexpr int kBatch = 8;
     for (int64_t wb = w1; wb <= w2; wb += kBatch) {
       float m[kBatch], l[kBatch];
       float4 v[kBatch];
