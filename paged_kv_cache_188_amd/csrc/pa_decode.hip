@@ -49,8 +49,8 @@
 //          (D/16)*col .. +D/16-1 of the token-major V pool (16 lanes read one
 //          V row); element nt of its four rows is the B operand of output
 //          tile nt.  Output: lane holds heads 4*grp + r, dims (D/16)*col + nt.
-//   pipeline: a ring of 4 tiles in registers, 3 in flight while one is
-//          computed.
+//   pipeline: each wave loads one tile, then attends to it; the 8 waves of a
+//          CU keep 8 tiles (64 KiB) in flight between them.
 //
 // Vector-ALU kernel (float32 K/V, or on request): 16-byte granules, LPR
 //   lanes per token, each group of LPR lanes an independent online-softmax
@@ -73,7 +73,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kDecodeWaves = 4;  // independent waves per workgroup
-constexpr int kRing = 4;         // 16-token tiles held in registers per wave (3 in flight)
 constexpr float kLazyMax = 8.f;  // headroom (log2) before the running max must move
 constexpr float kNegInf = -__builtin_inff();
 
@@ -147,23 +146,20 @@ struct Tile {
 
 // Load a tile whose 16 tokens lie in one block (BS >= 16): cb is the element
 // offset of the (block, KV head) chunk, o the tile's first token in the
-// block.  `past` marks a refill beyond the last tile: every lane of a load
-// instruction then reads the same granule at the chunk's start (one cache
-// line per instruction; distinct granules per instruction, so the compiler
-// cannot fold the loads into one and copy it) and the data is never used.
+// block.
 template <int D, int BS>
 __device__ __forceinline__ void load_tile(const uint16_t* kpool, const uint16_t* vpool, int64_t cb,
-                                          int o, bool past, int lane, Tile<D>& b) {
+                                          int o, int lane, Tile<D>& b) {
   constexpr int DV = D / 16;
   const int grp = lane >> 4, col = lane & 15;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s)
     b.k[s] = load_stream(reinterpret_cast<const uint4*>(
-        kpool + cb + (past ? 8 * s : ((int64_t)(4 * s + grp) * BS + o + col) * 8)));
+        kpool + cb + ((int64_t)(4 * s + grp) * BS + o + col) * 8));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     b.v[j] = load_stream(reinterpret_cast<const VRowT<D>*>(
-        vpool + cb + (past ? 8 * j : (int64_t)(o + 4 * grp + j) * D + DV * col)));
+        vpool + cb + (int64_t)(o + 4 * grp + j) * D + DV * col));
 }
 
 // Attend the G heads to one tile: `valid` (1..16) of its tokens are in the
@@ -253,8 +249,8 @@ __device__ __forceinline__ void compute_tile(const DecodeParams& p, MfmaState<D>
 
 // Tiles [tile_begin, tile_end) of segment (seq, kvh) whose context is n
 // tokens, accumulated into st (fixed-partition path).  The tiles may touch
-// at most 64 blocks (one block id per lane).  A ring of kRing tiles stays in
-// registers, kRing - 1 in flight while one is computed.
+// at most 64 blocks (one block id per lane).  One tile at a time: load, then
+// attend (the other waves of the CU keep the memory system busy meanwhile).
 template <int D, int BS>
 __device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int kvh, int n,
                                            int tile_begin, int tile_end,
@@ -284,11 +280,10 @@ __device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int k
   };
 
   auto load = [&](int t, Tile<D>& b) {
-    const bool past = t >= ntiles;
-    const int tb = start + 16 * min(t, ntiles - 1);
+    const int tb = start + 16 * t;
     if constexpr (BS >= 16) {
       load_tile<D, BS>(kpool, vpool, chunk_base(__builtin_amdgcn_readlane(my_id, tb / BS - b0)),
-                       tb % BS, past, lane, b);
+                       tb % BS, lane, b);
     } else {
       // a tile spans two blocks: each lane fetches its row's id with a shuffle
       auto blk_base = [&](int tok) -> int64_t {
@@ -300,28 +295,20 @@ __device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int k
 #pragma unroll
       for (int s = 0; s < D / 32; ++s)
         b.k[s] = load_stream(reinterpret_cast<const uint4*>(
-            kpool + kb + (past ? 0 : ((int64_t)(4 * s + grp) * BS + kt % BS) * 8)));
+            kpool + kb + ((int64_t)(4 * s + grp) * BS + kt % BS) * 8));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int vt = tb + 4 * grp + j;
         b.v[j] = load_stream(reinterpret_cast<const VRowT<D>*>(
-            vpool + blk_base(vt) + (past ? 0 : (int64_t)(vt % BS) * D + DV * col)));
+            vpool + blk_base(vt) + (int64_t)(vt % BS) * D + DV * col));
       }
     }
   };
 
-  // The first pass only fills the ring, so every path into a compute has
-  // issued the ring's loads in the same order (the compiler can then wait for
-  // the oldest tile alone).
-  Tile<D> ring[kRing];
-  for (int t0 = -kRing; t0 < ntiles; t0 += kRing) {
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      const int t = t0 + i;
-      if (t >= 0 && t < ntiles)
-        compute_tile<D>(p, st, qv, ring[i], min(16, end - (start + 16 * t)), lane);
-      load(t + kRing, ring[i]);
-    }
+  for (int t = 0; t < ntiles; ++t) {
+    Tile<D> b;
+    load(t, b);
+    compute_tile<D>(p, st, qv, b, min(16, end - (start + 16 * t)), lane);
   }
 }
 
@@ -547,23 +534,24 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
     }
   };
 
-  Tile<D> ring[kRing];
-  int ring_seg[kRing];
-  int ring_tv[kRing];
-
-  auto load = [&](int u, int i) {
-    const bool past = u >= ntiles;
-    const int uu = min(u, ntiles - 1);
-    if (uu / kWave != chunk) {  // entering the next chunk (its loads were issued a chunk ago)
-      chunk = uu / kWave;
-      dc = dn;  // loaded a chunk ago
+  // One tile at a time: its descriptor, a new segment's Q (issued before the
+  // tile, so it arrives with it), the tile's K/V, then the attention.  A wave
+  // keeps one tile in flight; the other waves of the CU overlap its compute.
+  // (Measured on MI355X: deeper per-wave pipelines -- rings of 2 to 4 tiles,
+  // or batches of 2 to 4 -- were slower: the extra requests in flight
+  // lengthen the queues without raising the bandwidth, and the waves finish
+  // further apart.)
+  for (int u = 0; u < ntiles; ++u) {
+    if (u / kWave != chunk) {  // entering the next chunk (its loads were issued a chunk ago)
+      chunk = u / kWave;
+      dc = dn;
       dc.settle();
       if ((chunk + 1) * kWave < ntiles) {
         dn = describe_tiles<BS>(p, s_prefix, next_pos, chunk_count(chunk + 1), lane);
         next_pos = advance(next_pos, kWave, s_prefix, S, Hkv);
       }
     }
-    const int l = uu % kWave;
+    const int l = u % kWave;
     const int seq = __builtin_amdgcn_readlane(dc.seq, l);
     const int kvh = __builtin_amdgcn_readlane(dc.kvh, l);
     const int t = __builtin_amdgcn_readlane(dc.t, l);
@@ -571,45 +559,18 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
     phys = (phys >= 0 && phys < p.num_blocks) ? phys : 0;  // a bad entry reads block 0
     const int n = min(max(__builtin_amdgcn_readlane(dc.n_raw, l), 0), p.max_tokens);
     const int seg = seq * Hkv + kvh;
-    const int tv = (t << 5) | min(16, n - 16 * t);
-    const int64_t cb = ((int64_t)phys * Hkv + kvh) * ((int64_t)BS * D);
-    load_tile<D, BS>(kpool, vpool, cb, (16 * (tv >> 5)) % BS, past, lane, ring[i]);
-    ring_seg[i] = past ? -1 : seg;
-    ring_tv[i] = tv;
-  };
-
-  auto compute = [&](int i) {
-    const int seg = ring_seg[i];
-    const int tv = ring_tv[i];
     if (seg != cur_seg) {
       if (cur_seg >= 0) finish_piece();
-      // Q of the new segment is read here, while the ring's loads stay in
-      // flight.  (Staging it earlier in spare registers costs register
-      // copies at the loop's join points, and a copy of a register with a
-      // pending load waits for that load.)
-      const int kvh = seg - (seg / Hkv) * Hkv;
-      mfma_load_q<D>(p, seg / Hkv, kvh * G, lane, qv);
-      // Q must be in registers on this rarely taken path: otherwise the wait
-      // for it lands where the paths join and drains every tile's loads.
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) asm volatile("" : "+v"(qv[s]));
+      mfma_load_q<D>(p, seq, kvh * G, lane, qv);
       st.reset();
       cur_seg = seg;
-      cur_t0 = tv >> 5;
+      cur_t0 = t;
     }
-    compute_tile<D>(p, st, qv, ring[i], tv & 31, lane);
-    cur_tlast = tv >> 5;
-  };
-
-  // The first pass only fills the ring, so every path into a compute has
-  // issued the ring's loads in the same order.
-  for (int u0 = -kRing; u0 < ntiles; u0 += kRing) {
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      const int u = u0 + i;
-      if (u >= 0 && u < ntiles) compute(i);
-      load(u + kRing, i);
-    }
+    Tile<D> b;
+    load_tile<D, BS>(kpool, vpool, ((int64_t)phys * Hkv + kvh) * ((int64_t)BS * D), (16 * t) % BS,
+                     lane, b);
+    compute_tile<D>(p, st, qv, b, min(16, n - 16 * t), lane);
+    cur_tlast = t;
   }
   finish_piece();
   if (lane == 0) *handoff = my_handoff;
