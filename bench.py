@@ -2,9 +2,10 @@
 """Benchmark of the paged KV-cache decode step on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the slot of every
-sequence's new token (pa_compute_slots), the KV write (pa_write_kv), the
-copy-on-write block copies when the workload has them (pa_copy_blocks), and
-paged decode attention (pa_decode_attention).  Inputs are resident in HBM
+sequence's new token and its K/V write (pa_write_kv_at: the slot computation
+and the write in one launch), the copy-on-write block copies when the
+workload has them (pa_copy_blocks), and paged decode attention
+(pa_decode_attention).  Inputs are resident in HBM
 before timing starts.  Each step reads a different one of several identical
 pool copies (together far larger than the 256 MB last-level cache), so no
 step is served from a cache warmed by the previous one.

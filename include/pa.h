@@ -6,6 +6,7 @@
  *
  *   pa_compute_slots     logical (sequence, position) -> physical cache slot
  *   pa_write_kv          store new tokens' K/V in their slots
+ *   pa_write_kv_at       the two above in one launch
  *   pa_copy_blocks       copy whole KV blocks (copy-on-write of shared blocks)
  *   pa_decode_attention  one query token per sequence attends to its history,
  *                        reached block by block through its block table
@@ -136,6 +137,27 @@ pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new,
                       int32_t num_blocks, int32_t block_size,
                       int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
                       void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_write_kv_at  (slots and write in one launch)
+ *
+ * pa_compute_slots followed by pa_write_kv, fused: token j goes to
+ *     slot = block_tables[i][p / block_size] * block_size + p % block_size
+ * with p = positions[j] and i = seq_ids[j] (or j when seq_ids is NULL), under
+ * exactly the rules of pa_compute_slots (slot -1, token skipped, for p < 0 or
+ * any index outside its table or the pool), and is stored as pa_write_kv
+ * stores it.  slots_out (int64 [num_tokens]) may be NULL; when given it
+ * receives the slots, so the call also does what pa_compute_slots does.
+ * Same element-type, stride and alignment rules as pa_write_kv.
+ * ------------------------------------------------------------------------- */
+pa_status pa_write_kv_at(void* k_cache, void* v_cache, const void* k_new,
+                         const void* v_new, const int32_t* block_tables,
+                         int32_t num_seqs, int32_t max_blocks_per_seq,
+                         const int32_t* seq_ids, const int32_t* positions,
+                         int32_t num_tokens, int64_t new_token_stride,
+                         int32_t num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                         int64_t* slots_out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * pa_copy_blocks  (copy-on-write)

@@ -37,6 +37,8 @@ SIGNATURES = {
     "pa_compute_slots": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P]),
     "pa_write_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
                                    ctypes.c_int, _P]),
+    "pa_write_kv_at": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I64, _I32,
+                                      _I32, _I32, _I32, ctypes.c_int, _P, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
     "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "pa_decode_streamk_workers": (_I32, [_I32, _I32, _I32, _I32, ctypes.c_int, ctypes.c_uint32]),
@@ -164,6 +166,33 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
     _check("pa_write_kv", lib().pa_write_kv(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), t,
         k_new.stride(0) if t else 0, nb, bs, hkv, d, _dtype_code(k_cache), _stream(stream)))
+
+
+def write_kv_at(k_cache, v_cache, k_new, v_new, block_tables, positions, seq_ids=None,
+                slots_out=None, stream=None):
+    """compute_slots + write_kv in one launch: token j goes to the slot of
+    (seq_ids[j] or j, positions[j]); the slots are also written to
+    ``slots_out`` when given."""
+    import torch
+    nb, hkv, bs, d = _pools(k_cache, v_cache)
+    _need(block_tables, torch.int32, "block_tables")
+    _need(positions, torch.int32, "positions")
+    if seq_ids is not None:
+        _need(seq_ids, torch.int32, "seq_ids")
+    if slots_out is not None:
+        _need(slots_out, torch.int64, "slots_out")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise TypeError("new K/V must have the pool's element type")
+    t = positions.numel()
+    if k_new.shape[0] != t or v_new.shape != k_new.shape or tuple(k_new.shape[1:]) != (hkv, d):
+        raise ValueError("k_new/v_new must be [T][Hkv][D] matching positions")
+    if t and (k_new.stride(2) != 1 or k_new.stride(1) != d or v_new.stride() != k_new.stride()):
+        raise ValueError("k_new/v_new rows must be contiguous [Hkv][D] with one token stride")
+    s, mb = block_tables.shape
+    _check("pa_write_kv_at", lib().pa_write_kv_at(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables), s, mb,
+        _ptr(seq_ids), _ptr(positions), t, k_new.stride(0) if t else 0, nb, bs, hkv, d,
+        _dtype_code(k_cache), _ptr(slots_out), _stream(stream)))
 
 
 def copy_blocks(k_cache, v_cache, block_mapping, stream=None):

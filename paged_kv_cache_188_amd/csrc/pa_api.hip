@@ -128,6 +128,33 @@ pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const voi
                                       head_dim * e, static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_write_kv_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                         const int32_t* block_tables, int32_t num_seqs,
+                         int32_t max_blocks_per_seq, const int32_t* seq_ids,
+                         const int32_t* positions, int32_t num_tokens, int64_t new_token_stride,
+                         int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, pa_dtype dtype, int64_t* slots_out, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      num_kv_heads < 1)
+    return PA_ERR_SHAPE;
+  if (!supported_block_size(block_size) || !supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (new_token_stride == 0) new_token_stride = row;
+  if (new_token_stride < row) return PA_ERR_SHAPE;
+  const int e = elem_bytes(dtype);
+  if ((new_token_stride * e) % 16) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !positions || (num_seqs > 0 && !block_tables))
+    return PA_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return PA_ERR_UNSUPPORTED;
+  return from_hip(pa::launch_write_kv_at(
+      k_cache, v_cache, k_new, v_new, block_tables, num_seqs, max_blocks_per_seq, seq_ids,
+      positions, slots_out, num_tokens, new_token_stride * e, num_blocks, block_size,
+      num_kv_heads, head_dim * e, static_cast<hipStream_t>(stream)));
+}
+
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
                          int32_t num_pairs, int32_t num_blocks, int32_t block_size,
                          int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype, void* stream) {

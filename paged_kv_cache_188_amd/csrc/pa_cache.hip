@@ -19,12 +19,12 @@
 namespace pa {
 namespace {
 
-__global__ __launch_bounds__(256) void compute_slots_kernel(
-    int64_t* __restrict__ slots, const int32_t* __restrict__ block_tables, int num_seqs,
-    int max_blocks_per_seq, const int32_t* __restrict__ seq_ids,
-    const int32_t* __restrict__ positions, int num_tokens, int block_size, int num_blocks) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= num_tokens) return;
+// Slot of token j (-1: padding, or an index outside its table or the pool).
+__device__ __forceinline__ int64_t token_slot(const int32_t* __restrict__ block_tables,
+                                              int num_seqs, int max_blocks_per_seq,
+                                              const int32_t* __restrict__ seq_ids,
+                                              const int32_t* __restrict__ positions, int j,
+                                              int block_size, int num_blocks) {
   const int p = positions[j];
   const int i = seq_ids ? seq_ids[j] : j;
   int64_t slot = -1;
@@ -36,24 +36,31 @@ __global__ __launch_bounds__(256) void compute_slots_kernel(
         slot = (int64_t)phys * block_size + (p - b * block_size);
     }
   }
-  slots[j] = slot;
+  return slot;
+}
+
+__global__ __launch_bounds__(256) void compute_slots_kernel(
+    int64_t* __restrict__ slots, const int32_t* __restrict__ block_tables, int num_seqs,
+    int max_blocks_per_seq, const int32_t* __restrict__ seq_ids,
+    const int32_t* __restrict__ positions, int num_tokens, int block_size, int num_blocks) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= num_tokens) return;
+  slots[j] = token_slot(block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions, j,
+                        block_size, num_blocks);
 }
 
 // One wave per token; each lane moves 16-byte granules of the token's
 // [Hkv][D] row to their places in the two pools.
 constexpr int kWriteWaves = 4;
 
-__global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_kernel(
-    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
-    const int64_t* __restrict__ slot_mapping, int num_tokens, int64_t token_stride_bytes,
-    int64_t pool_slots, int block_size, int num_kv_heads, int head_chunks) {
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int j = blockIdx.x * kWriteWaves + wave;
-  if (j >= num_tokens) return;
-  const int64_t slot = slot_mapping[j];
-  if (slot < 0 || slot >= pool_slots) return;  // padding token, or outside the pool
+// Token j's K and V rows into slot `slot` of the two pools (one wave).
+__device__ __forceinline__ void write_token(uint8_t* __restrict__ k_cache,
+                                            uint8_t* __restrict__ v_cache,
+                                            const uint8_t* __restrict__ k_new,
+                                            const uint8_t* __restrict__ v_new, int j,
+                                            int64_t slot, int64_t token_stride_bytes,
+                                            int block_size, int num_kv_heads, int head_chunks,
+                                            int lane) {
   const int64_t blk = slot / block_size;
   const int64_t off = slot - blk * block_size;
   const int nchunks = num_kv_heads * head_chunks;
@@ -69,6 +76,42 @@ __global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_kernel(
     *reinterpret_cast<uint4*>(k_cache + kdst) = a;
     *reinterpret_cast<uint4*>(v_cache + vdst) = b;
   }
+}
+
+__global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int64_t token_stride_bytes,
+    int64_t pool_slots, int block_size, int num_kv_heads, int head_chunks) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int j = blockIdx.x * kWriteWaves + wave;
+  if (j >= num_tokens) return;
+  const int64_t slot = slot_mapping[j];
+  if (slot < 0 || slot >= pool_slots) return;  // padding token, or outside the pool
+  write_token(k_cache, v_cache, k_new, v_new, j, slot, token_stride_bytes, block_size,
+              num_kv_heads, head_chunks, lane);
+}
+
+// The slot computation and the write in one launch (one wave per token); the
+// slots are also stored when `slots_out` is given.
+__global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_at_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int32_t* __restrict__ block_tables, int num_seqs, int max_blocks_per_seq,
+    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions,
+    int64_t* __restrict__ slots_out, int num_tokens, int64_t token_stride_bytes, int num_blocks,
+    int block_size, int num_kv_heads, int head_chunks) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int j = blockIdx.x * kWriteWaves + wave;
+  if (j >= num_tokens) return;
+  const int64_t slot = token_slot(block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions,
+                                  j, block_size, num_blocks);
+  if (slots_out && lane == 0) slots_out[j] = slot;
+  if (slot < 0) return;  // padding token, or an index outside its table or the pool
+  write_token(k_cache, v_cache, k_new, v_new, j, slot, token_stride_bytes, block_size,
+              num_kv_heads, head_chunks, lane);
 }
 
 // grid = (pair, pool K/V, 16 KiB piece of the block).  Each thread moves up
@@ -128,6 +171,23 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
                      static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
                      slot_mapping, num_tokens, token_stride_bytes,
                      (int64_t)num_blocks * block_size, block_size, num_kv_heads, head_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_kv_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                              const int32_t* block_tables, int num_seqs, int max_blocks_per_seq,
+                              const int32_t* seq_ids, const int32_t* positions,
+                              int64_t* slots_out, int num_tokens, int64_t token_stride_bytes,
+                              int num_blocks, int block_size, int num_kv_heads, int head_bytes,
+                              hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int grid = (num_tokens + kWriteWaves - 1) / kWriteWaves;
+  hipLaunchKernelGGL(write_kv_at_kernel, dim3(grid), dim3(kWriteWaves * kWave), 0, stream,
+                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                     static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
+                     block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions, slots_out,
+                     num_tokens, token_stride_bytes, num_blocks, block_size, num_kv_heads,
+                     head_bytes / 16);
   return hipGetLastError();
 }
 

@@ -22,6 +22,13 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
                            int num_blocks, int block_size, int num_kv_heads, int row_bytes,
                            hipStream_t stream);
 
+hipError_t launch_write_kv_at(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                              const int32_t* block_tables, int num_seqs, int max_blocks_per_seq,
+                              const int32_t* seq_ids, const int32_t* positions,
+                              int64_t* slots_out, int num_tokens, int64_t token_stride_bytes,
+                              int num_blocks, int block_size, int num_kv_heads, int head_bytes,
+                              hipStream_t stream);
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
                               int num_pairs, int num_blocks, int64_t block_bytes,
                               hipStream_t stream);

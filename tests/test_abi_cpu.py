@@ -150,6 +150,23 @@ def test_write_copy_slots_validation(lib):
     assert w(kn=NULL) == NUL
     assert w(kn=MISALIGNED) == UNSUP
     assert w(T=0, kc=NULL, vc=NULL, kn=NULL, vn=NULL, sl=NULL) == OK
+    wa = lambda **k: lib.pa_write_kv_at(k.get("kc", FAKE), k.get("vc", FAKE), k.get("kn", FAKE),
+                                        k.get("vn", FAKE), k.get("bt", FAKE), k.get("S", 2),
+                                        k.get("MB", 3), k.get("sid", NULL), k.get("pos", FAKE),
+                                        k.get("T", 3), k.get("stride", 0), k.get("NB", 4),
+                                        k.get("bs", 16), k.get("Hkv", 2), k.get("D", 128),
+                                        k.get("dtype", 1), k.get("out", NULL), NULL)
+    assert wa(dtype=9) == DTYPE
+    assert wa(T=-1) == SHAPE
+    assert wa(MB=0) == SHAPE
+    assert wa(bs=24) == UNSUP
+    assert wa(D=48) == UNSUP
+    assert wa(stride=100) == SHAPE
+    assert wa(stride=260) == UNSUP
+    assert wa(pos=NULL) == NUL
+    assert wa(bt=NULL) == NUL
+    assert wa(vn=MISALIGNED) == UNSUP
+    assert wa(T=0, kc=NULL, vc=NULL, kn=NULL, vn=NULL, bt=NULL, pos=NULL) == OK
     c = lambda **k: lib.pa_copy_blocks(k.get("kc", FAKE), k.get("vc", FAKE), k.get("map", FAKE),
                                        k.get("n", 2), k.get("NB", 4), k.get("bs", 16),
                                        k.get("Hkv", 2), k.get("D", 64), k.get("dtype", 0), NULL)

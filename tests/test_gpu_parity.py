@@ -34,14 +34,17 @@ def _device():
 
 
 def run_both(wl, *, partition=None, vector_only=False, seqs=None, heads=None,
-             check_pools=True):
+             check_pools=True, fused_write=True):
     """Run the plan on the GPU and in the oracle; check slots and pools
-    bit-exactly; return (gpu_out, oracle_out)."""
+    bit-exactly; return (gpu_out, oracle_out).  Writes go through
+    pa_write_kv_at, or pa_compute_slots + pa_write_kv with fused_write=False."""
     DeviceWorkload = _device()
-    _say(f"[case] {wl.name} partition={partition} vector_only={vector_only}")
+    _say(f"[case] {wl.name} partition={partition} vector_only={vector_only} "
+         f"fused_write={fused_write}")
     dev = DeviceWorkload(wl)
-    dev.run_setup()
-    out = dev.run_step(partition_size=partition, vector_only=vector_only).cpu().numpy()
+    dev.run_setup(fused_write=fused_write)
+    out = dev.run_step(partition_size=partition, vector_only=vector_only,
+                       fused_write=fused_write).cpu().numpy()
     torch.cuda.synchronize()
     kp, vp, ref, slots_ref = run_oracle(wl, wl.setup + wl.step, seqs=seqs, heads=heads)
     got_slots = dev.slots_of(dev.setup_ops + dev.step_ops)
@@ -66,6 +69,15 @@ def test_workload_parity_small(cid):
     err = max_abs_err(out, ref)
     _say(f"  max_abs_err={err:.3e}")
     assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("cid", [1, 4])
+def test_separate_slot_and_write_calls(cid):
+    """pa_compute_slots + pa_write_kv (two launches) give the same slots and
+    pools as the fused pa_write_kv_at, bit for bit."""
+    wl = W.make(cid, small=(cid != 1))
+    out, ref = run_both(wl, fused_write=False)
+    assert max_abs_err(out, ref) <= TOL[wl.dtype]
 
 
 def test_cow_observable_parity():

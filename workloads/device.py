@@ -77,12 +77,19 @@ class DeviceWorkload:
         return self.workspace
 
     # -------------------------------------------------------------------
-    def _run(self, ops, pool=0, partition_size=None, vector_only=False, stream=None):
+    def _run(self, ops, pool=0, partition_size=None, vector_only=False, stream=None,
+             fused_write=True):
+        """Run `ops`.  A write is one pa_write_kv_at launch (slots computed and
+        stored in the same kernel) or, with fused_write=False, pa_compute_slots
+        followed by pa_write_kv."""
         wl = self.wl
         k, v = self.pools[pool]
         part = wl.partition_size if partition_size is None else partition_size
         for kind, x in ops:
-            if kind == "write":
+            if kind == "write" and fused_write:
+                pa.write_kv_at(k, v, x["k"], x["v"], self.tables[x["table"]], x["positions"],
+                               seq_ids=x["seq_ids"], slots_out=x["slots"], stream=stream)
+            elif kind == "write":
                 pa.compute_slots(self.tables[x["table"]], x["positions"], wl.block_size,
                                  wl.num_blocks, seq_ids=x["seq_ids"], out=x["slots"],
                                  stream=stream)
@@ -96,8 +103,8 @@ class DeviceWorkload:
                                     vector_only=vector_only, stream=stream)
         return self.out
 
-    def run_setup(self, pool=0):
-        self._run(self.setup_ops, pool)
+    def run_setup(self, pool=0, **kw):
+        self._run(self.setup_ops, pool, **kw)
 
     def run_step(self, pool=0, **kw):
         return self._run(self.step_ops, pool, **kw)
