@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the paged KV-cache decode step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: the slot of every
-sequence's new token and its K/V write (pa_write_kv_at: the slot computation
-and the write in one launch), the copy-on-write block copies when the
-workload has them (pa_copy_blocks), and paged decode attention
-(pa_decode_attention).  Inputs are resident in HBM
+A step is one pass of the whole hot path over one batch: the copy-on-write
+block copies when the workload has them (pa_copy_blocks), then every
+sequence's new token stored in its slot and paged decode attention over the
+whole context (pa_decode_attention_append: slot computation, KV write and
+attention in one call).  --separate runs the same step as pa_write_kv_at
+followed by pa_decode_attention.  Inputs are resident in HBM
 before timing starts.  Each step reads a different one of several identical
 pool copies (together far larger than the 256 MB last-level cache), so no
 step is served from a cache warmed by the previous one.
@@ -45,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition", type=int, default=None,
                     help="decode partition size (default: the workload's / the library's choice)")
+    ap.add_argument("--separate", action="store_true",
+                    help="store the new tokens with pa_write_kv_at, then pa_decode_attention")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run pa_copy_blocks over a known number of bytes (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -163,16 +166,18 @@ def main():
     dev.add_pool_copies(npools - 1)
     torch.cuda.synchronize()
 
-    decode_ops = [op for op in dev.step_ops if op[0] == "decode"]
-    other_ops = [op for op in dev.step_ops if op[0] != "decode"]
+    ops = dev.step_ops if args.separate else dev.step_ops_append
+    appended = any(kind == "decode_append" for kind, _ in ops)
+    decode_ops = [op for op in ops if op[0] in ("decode", "decode_append")]
+    other_ops = [op for op in ops if op[0] not in ("decode", "decode_append")]
     stream = torch.cuda.current_stream()
 
     def step(k, ev=None):
         pool = k % npools
-        dev._run(other_ops, pool)
+        dev._run(other_ops, pool, record_slots=False)
         if ev is not None:
             ev[0].record(stream)
-        dev._run(decode_ops, pool)
+        dev._run(decode_ops, pool, record_slots=False)
         if ev is not None:
             ev[1].record(stream)
 
@@ -190,18 +195,23 @@ def main():
     ms_step = wall * 1e3 / args.steps
     workers = pa.decode_streamk_workers(wl.num_seqs, wl.head_dim, wl.block_size,
                                         wl.partition_size, dev.torch_dtype)
+    call = "pa_decode_attention_append" if appended else "pa_decode_attention"
     if workers > 0:
         decomposition = {"path": "stream-K", "persistent_waves": workers}
-        kernel = ("pa_decode_attention: decode_mfma_streamk_kernel + decode_streamk_merge_kernel "
+        kernel = (f"{call}: decode_mfma_streamk_kernel + decode_streamk_merge_kernel "
                   "(events around the call)")
     else:
         decomposition = {"path": "fixed partitions", "partition_size": pa.decode_partition_size(
             wl.num_seqs, wl.num_kv_heads, wl.block_size, wl.max_context_len, wl.partition_size)}
-        kernel = "pa_decode_attention: decode_mfma_kernel + decode_reduce_kernel (events around the call)"
+        kernel = (f"{call}: " + ("append_kv_kernel + " if appended else "")
+                  + "decode_mfma_kernel + decode_reduce_kernel (events around the call)")
     dec_ms = [a.elapsed_time(b) for a, b in events]
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     kv_bytes = wl.kv_bytes_read()
     dec_bytes = wl.decode_bytes()
+    if appended:  # the call also stores every non-empty sequence's new K/V row
+        dec_bytes += int((wl.context_lens > 0).sum()) * wl.num_kv_heads * wl.head_dim * 2 \
+            * (2 if wl.dtype == "bf16" else 4)
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     res = {
@@ -225,6 +235,10 @@ def main():
             "sum_context_tokens": int(wl.context_lens.sum()),
             "max_context_len": wl.max_context_len,
             "decomposition": decomposition,
+            "step_calls": [{"copy": "pa_copy_blocks", "write": "pa_write_kv_at",
+                            "decode": "pa_decode_attention",
+                            "decode_append": "pa_decode_attention_append"}[kind]
+                           for kind, _ in ops],
             "seed": list(wl.seed), "pool_copies_rotated": npools,
             "parallelism": "single GPU",
         },

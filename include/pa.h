@@ -10,6 +10,7 @@
  *   pa_copy_blocks       copy whole KV blocks (copy-on-write of shared blocks)
  *   pa_decode_attention  one query token per sequence attends to its history,
  *                        reached block by block through its block table
+ *   pa_decode_attention_append  the new tokens stored and attended in one call
  *
  * Sources, cited by page title and section:
  *   [nalar]    "PagedAttention: memetakan blok KV logis ke memori fisik tidak
@@ -245,6 +246,39 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache,
                               int32_t partition_size, void* workspace,
                               size_t workspace_bytes, pa_dtype dtype,
                               uint32_t flags, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode_attention_append  (write the new tokens, then attend)
+ *
+ * The decode step of [gyaansetu] "Apa itu KV Cache?": each sequence's new
+ * token is stored in the cache and attended together with its history.  For
+ * every sequence i with 1 <= context_lens[i] <= max_blocks_per_seq *
+ * block_size, row i of k_new / v_new ([num_seqs][num_kv_heads][head_dim],
+ * token stride new_token_stride elements, 0 = num_kv_heads*head_dim) is the
+ * token at position context_lens[i]-1.  Results equal
+ *     pa_write_kv_at(positions[i] = context_lens[i]-1, seq_ids = NULL)
+ *     followed by pa_decode_attention with the same arguments:
+ * the row is stored at its slot (skipped, as there, when the table entry is
+ * outside the pool) and the output attends over positions
+ * 0 .. context_lens[i]-1 with the new token's K/V taken from k_new / v_new.
+ * Rows of sequences with an empty context are not read.  On the stream-K
+ * path the decode kernel itself reads the new rows and stores them (one
+ * launch fewer); on the fixed-partition path the rows are stored first.
+ * Workspace, decomposition, errors and determinism as pa_decode_attention;
+ * k_new / v_new must be 16-byte aligned with 16-byte token strides.
+ * ------------------------------------------------------------------------- */
+pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache,
+                                     void* v_cache, const void* k_new,
+                                     const void* v_new, int64_t new_token_stride,
+                                     const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, int32_t max_blocks_per_seq,
+                                     int32_t max_context_len, float scale,
+                                     int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, pa_dtype dtype,
+                                     uint32_t flags, void* stream);
 
 /* Text of a status code (static storage). */
 const char* pa_status_string(pa_status status);

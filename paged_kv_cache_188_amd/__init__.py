@@ -47,6 +47,10 @@ SIGNATURES = {
     "pa_decode_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                            _I32, _I32, _I32, ctypes.c_float, _I32, _P,
                                            ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32, _P]),
+    "pa_decode_attention_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I32,
+                                                  _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                  ctypes.c_float, _I32, _P, ctypes.c_size_t,
+                                                  ctypes.c_int, ctypes.c_uint32, _P]),
 }
 
 
@@ -232,9 +236,13 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
 
 
 def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-                     partition_size=0, workspace=None, out=None, vector_only=False, stream=None):
+                     partition_size=0, workspace=None, out=None, vector_only=False, stream=None,
+                     k_new=None, v_new=None):
     """Paged decode attention; returns float32 [S][Hq][D].  ``workspace`` (a
-    uint8 device tensor) is allocated here when not given."""
+    uint8 device tensor) is allocated here when not given.  With ``k_new`` /
+    ``v_new`` ([S][Hkv][D]) each sequence's new token (position ctx-1) is
+    stored in the pools and attended in the same call
+    (pa_decode_attention_append)."""
     import torch
     s, hq, d = q.shape
     nb, hkv, bs, d2 = _pools(k_cache, v_cache)
@@ -251,6 +259,21 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max
     if out is None:
         out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
+    if k_new is not None:
+        if v_new is None or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+            raise TypeError("k_new and v_new must both be given, with the pool's element type")
+        if k_new.shape != (s, hkv, d) or v_new.shape != k_new.shape:
+            raise ValueError("k_new/v_new must be [S][Hkv][D]")
+        if k_new.stride(2) != 1 or k_new.stride(1) != d or v_new.stride() != k_new.stride():
+            raise ValueError("k_new/v_new rows must be contiguous [Hkv][D] with one token stride")
+        _check("pa_decode_attention_append", lib().pa_decode_attention_append(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+            k_new.stride(0), _ptr(block_tables), _ptr(context_lens), s, hq, hkv, d, bs, nb, mb,
+            int(max_context_len), float(scale), int(partition_size),
+            _ptr(workspace) if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, _dtype_code(k_cache),
+            PA_DECODE_VECTOR_ONLY if vector_only else 0, _stream(stream)))
+        return out
     _check("pa_decode_attention", lib().pa_decode_attention(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), s, hq, hkv, d, bs, nb, mb, int(max_context_len), float(scale),

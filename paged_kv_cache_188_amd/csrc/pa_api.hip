@@ -208,13 +208,18 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   return pa::decode_workspace_partition(num_seqs, num_q_heads, head_dim, (int)P).total;
 }
 
-pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* block_tables, const int32_t* context_lens,
-                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                              int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
-                              int32_t partition_size, void* workspace, size_t workspace_bytes,
-                              pa_dtype dtype, uint32_t flags, void* stream) {
+namespace {
+
+// Decode, optionally with each sequence's new token appended first (k_new
+// non-null): shared by pa_decode_attention and pa_decode_attention_append.
+pa_status decode_impl(float* out, const void* q, const void* k_cache, const void* v_cache,
+                      const void* k_new, const void* v_new, int64_t new_token_stride,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, float scale, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, pa_dtype dtype, uint32_t flags,
+                      bool append, void* stream) {
   if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1 || max_context_len < 0 || num_q_heads % num_kv_heads)
@@ -245,6 +250,15 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, co
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_UNSUPPORTED;
+  const int e = elem_bytes(dtype);
+  if (append) {
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (new_token_stride == 0) new_token_stride = row;
+    if (new_token_stride < row) return PA_ERR_SHAPE;
+    if ((new_token_stride * e) % 16) return PA_ERR_UNSUPPORTED;
+    if (!k_new || !v_new) return PA_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_UNSUPPORTED;
+  }
 
   pa::DecodeParams p{};
   p.out = out;
@@ -267,7 +281,9 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, co
   p.group = num_q_heads / num_kv_heads;
   p.num_blocks = num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
+  p.block_size = block_size;
   p.scale_log2 = scale * 1.4426950408889634f;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (path == pa::DecodePath::kStreamK) {
     int workers = 0;
     if (streamk_workers(head_dim, &workers) != 0) return PA_ERR_HIP;
@@ -275,13 +291,55 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, co
     p.partition = 16;
     p.max_partitions = 1;
     p.max_tokens = max_tokens;
+    if (append) {  // the decode kernel appends the new tokens itself
+      p.k_new = k_new;
+      p.v_new = v_new;
+      p.new_stride = new_token_stride;
+    }
   } else {
     p.partition = part;
     p.max_partitions = (int)P;
     p.max_tokens = (int)((int64_t)P * part < max_tokens ? (int64_t)P * part : max_tokens);
+    if (append) {  // store the new tokens first, then attend
+      const pa_status st = from_hip(pa::launch_append_kv(
+          const_cast<void*>(k_cache), const_cast<void*>(v_cache), k_new, v_new,
+          new_token_stride * e, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+          num_blocks, block_size, num_kv_heads, head_dim * e, hs));
+      if (st != PA_OK) return st;
+    }
   }
-  return from_hip(pa::launch_decode(p, head_dim, block_size, dtype, vector_only, path,
-                                    static_cast<hipStream_t>(stream)));
+  return from_hip(pa::launch_decode(p, head_dim, block_size, dtype, vector_only, path, hs));
+}
+
+}  // namespace
+
+pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                              int32_t partition_size, void* workspace, size_t workspace_bytes,
+                              pa_dtype dtype, uint32_t flags, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, 0, block_tables, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                     workspace_bytes, dtype, flags, false, stream);
+}
+
+pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache, void* v_cache,
+                                     const void* k_new, const void* v_new,
+                                     int64_t new_token_stride, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, pa_dtype dtype, uint32_t flags,
+                                     void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, k_new, v_new, new_token_stride, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
+                     workspace, workspace_bytes, dtype, flags, true, stream);
 }
 
 }  // extern "C"

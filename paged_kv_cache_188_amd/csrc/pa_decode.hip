@@ -146,20 +146,27 @@ struct Tile {
 
 // Load a tile whose 16 tokens lie in one block (BS >= 16): cb is the element
 // offset of the (block, KV head) chunk, o the tile's first token in the
-// block.
+// block.  If kk >= 0, token kk of the tile is read from the row pair knew /
+// vnew (D elements each) instead of the pools.
 template <int D, int BS>
 __device__ __forceinline__ void load_tile(const uint16_t* kpool, const uint16_t* vpool, int64_t cb,
-                                          int o, int lane, Tile<D>& b) {
+                                          int o, int lane, Tile<D>& b,
+                                          const uint16_t* knew = nullptr,
+                                          const uint16_t* vnew = nullptr, int kk = -1) {
   constexpr int DV = D / 16;
   const int grp = lane >> 4, col = lane & 15;
+  const bool k_from_new = col == kk;  // kk = -1: no token is overridden
 #pragma unroll
   for (int s = 0; s < D / 32; ++s)
     b.k[s] = load_stream(reinterpret_cast<const uint4*>(
-        kpool + cb + ((int64_t)(4 * s + grp) * BS + o + col) * 8));
+        k_from_new ? knew + 32 * s + 8 * grp
+                   : kpool + cb + ((int64_t)(4 * s + grp) * BS + o + col) * 8));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 4; ++j) {
+    const bool v_from_new = 4 * grp + j == kk;
     b.v[j] = load_stream(reinterpret_cast<const VRowT<D>*>(
-        vpool + cb + (int64_t)(o + 4 * grp + j) * D + DV * col));
+        v_from_new ? vnew + DV * col : vpool + cb + (int64_t)(o + 4 * grp + j) * D + DV * col));
+  }
 }
 
 // Attend the G heads to one tile: `valid` (1..16) of its tokens are in the
@@ -432,6 +439,13 @@ struct TileDescs {
   }
 };
 
+// The tile's raw context length is its clamped one (so position n-1 really
+// is the sequence's last token).
+__device__ __forceinline__ bool n_raw_ok(const TileDescs& d, int l, const DecodeParams& p) {
+  const int n = __builtin_amdgcn_readlane(d.n_raw, l);
+  return n >= 1 && n <= p.max_tokens;
+}
+
 template <int BS>
 __device__ __forceinline__ TileDescs describe_tiles(const DecodeParams& p, const int* s_prefix,
                                                     Pos start, int count, int lane) {
@@ -566,10 +580,18 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
       cur_seg = seg;
       cur_t0 = t;
     }
+    const int64_t cb = ((int64_t)phys * Hkv + kvh) * ((int64_t)BS * D);
+    const int valid = min(16, n - 16 * t);
+    // The tile holding the sequence's new token (position n-1) when the call
+    // appends: that token is read from the new rows (the merge kernel stores
+    // them into their slots, so no wave here waits for a store).
+    const bool append = p.k_new != nullptr && valid == n - 16 * t && n_raw_ok(dc, l, p);
+    const int64_t row = (int64_t)seq * p.new_stride + (int64_t)kvh * D;
     Tile<D> b;
-    load_tile<D, BS>(kpool, vpool, ((int64_t)phys * Hkv + kvh) * ((int64_t)BS * D), (16 * t) % BS,
-                     lane, b);
-    compute_tile<D>(p, st, qv, b, min(16, n - 16 * t), lane);
+    load_tile<D, BS>(kpool, vpool, cb, (16 * t) % BS, lane, b,
+                     static_cast<const uint16_t*>(p.k_new) + row,
+                     static_cast<const uint16_t*>(p.v_new) + row, append ? valid - 1 : -1);
+    compute_tile<D>(p, st, qv, b, valid, lane);
     cur_tlast = t;
   }
   finish_piece();
@@ -583,6 +605,36 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeParams p) {
   constexpr int C = D / 4;  // float4 chunks per row
   const int G = p.group;
+  if (blockIdx.x >= p.max_workers) {
+    // Workgroups past the wave slots store the appended tokens: 8 (sequence,
+    // KV head) rows per workgroup, 32 threads per row (16 K granules, 16 V
+    // granules of 16 bytes for D = 128; half of them for D = 64).
+    const int64_t r = (int64_t)(blockIdx.x - p.max_workers) * 8 + threadIdx.x / 32;
+    const int c = threadIdx.x % 32;
+    constexpr int kChunks = D / 8;  // 16-byte granules per row
+    if (r >= (int64_t)p.num_seqs * p.num_kv_heads || c % 16 >= kChunks) return;
+    const int seq = (int)(r / p.num_kv_heads), kvh = (int)(r % p.num_kv_heads);
+    const int n = p.context_lens[seq];
+    if (n < 1 || n > p.max_tokens) return;
+    const int pos = n - 1;
+    const int bs = p.block_size;
+    const int phys = p.block_tables[(int64_t)seq * p.max_blocks_per_seq + pos / bs];
+    if (phys < 0 || phys >= p.num_blocks) return;
+    const int o = pos % bs;
+    const int64_t cb = ((int64_t)phys * p.num_kv_heads + kvh) * ((int64_t)bs * D);
+    const int64_t row = (int64_t)seq * p.new_stride + (int64_t)kvh * D;
+    const int w = c % 16;
+    if (c < 16) {
+      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k_new) + row + 8 * w);
+      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.k_cache)) +
+                                cb + ((int64_t)w * bs + o) * 8) = x;
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v_new) + row + 8 * w);
+      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.v_cache)) +
+                                cb + (int64_t)o * D + 8 * w) = x;
+    }
+    return;
+  }
   const int64_t w1 = blockIdx.x;
   const int2 h = reinterpret_cast<const int2*>(p.ws_handoff)[w1];
   if (h.x < 0) return;
@@ -894,8 +946,11 @@ hipError_t launch_streamk(const DecodeParams& p, hipStream_t stream) {
                      dim3(kDecodeWaves * kWave), lds, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_streamk_merge_kernel<D>), dim3(blocks * kDecodeWaves), dim3(256), 0,
-                     stream, p);
+  // merge workgroups (one per wave slot), then the append workgroups
+  const int64_t append_rows = p.k_new ? (int64_t)p.num_seqs * p.num_kv_heads : 0;
+  const int64_t grid = (int64_t)blocks * kDecodeWaves + (append_rows + 7) / 8;
+  hipLaunchKernelGGL((decode_streamk_merge_kernel<D>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

@@ -29,6 +29,15 @@ hipError_t launch_write_kv_at(void* k_cache, void* v_cache, const void* k_new, c
                               int num_blocks, int block_size, int num_kv_heads, int head_bytes,
                               hipStream_t stream);
 
+// Store row i of k_new / v_new at position context_lens[i]-1 of sequence i
+// (skipped for an empty context, a context beyond max_blocks*block_size, or
+// an invalid table entry).  One wave per sequence.
+hipError_t launch_append_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            int64_t token_stride_bytes, const int32_t* block_tables,
+                            const int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
+                            int num_blocks, int block_size, int num_kv_heads, int head_bytes,
+                            hipStream_t stream);
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
                               int num_pairs, int num_blocks, int64_t block_bytes,
                               hipStream_t stream);
@@ -47,12 +56,20 @@ struct DecodeParams {
   float* ws_acc;      // unnormalised outputs
   int32_t* ws_handoff; // stream-K: [max_workers][2] per wave {segment it hands on, last wave
                        // sharing it} or {-1, -1}; every launched wave writes its entry
+  // stream-K with the new token appended in the same launch (else null): row
+  // i of k_new / v_new ([S][Hkv][D], token stride new_stride elements) is
+  // sequence i's token at position ctx-1; it is attended from these rows and
+  // stored into its cache slot
+  const void* k_new;
+  const void* v_new;
+  int64_t new_stride;
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
   int group;          // num_q_heads / num_kv_heads
   int num_blocks;
   int max_blocks_per_seq;
+  int block_size;
   int partition;      // fixed-partition path: tokens per partition
   int max_partitions; // fixed-partition path: P = ceil(max_context_len / partition)
   int max_tokens;     // every context length is clamped to it, so no index leaves its buffer

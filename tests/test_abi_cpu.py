@@ -97,6 +97,17 @@ def test_decode_validation(lib):
     assert _decode(lib, part=16, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == WS   # alignment
     # zero sequences: nothing to do, no HIP call
     assert _decode(lib, S=0, out=NULL, q=NULL) == OK
+    # the append variant: same checks plus its new rows
+    ap = lambda **k: lib.pa_decode_attention_append(
+        k.get("out", FAKE), FAKE, FAKE, FAKE, k.get("kn", FAKE), k.get("vn", FAKE),
+        k.get("stride", 0), FAKE, FAKE, 2, 8, 2, 128, 16, 10, 4, 40, 0.1, k.get("part", 64),
+        NULL, 0, k.get("dtype", 1), 0, NULL)
+    assert ap(dtype=4) == DTYPE
+    assert ap(kn=NULL) == NUL
+    assert ap(vn=MISALIGNED) == UNSUP
+    assert ap(stride=100) == SHAPE
+    assert ap(stride=260) == UNSUP
+    assert ap(out=NULL) == NUL
 
 
 def test_workspace_and_partition_rules(lib):

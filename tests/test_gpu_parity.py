@@ -34,17 +34,21 @@ def _device():
 
 
 def run_both(wl, *, partition=None, vector_only=False, seqs=None, heads=None,
-             check_pools=True, fused_write=True):
+             check_pools=True, fused_write=True, append=False):
     """Run the plan on the GPU and in the oracle; check slots and pools
     bit-exactly; return (gpu_out, oracle_out).  Writes go through
-    pa_write_kv_at, or pa_compute_slots + pa_write_kv with fused_write=False."""
+    pa_write_kv_at, or pa_compute_slots + pa_write_kv with fused_write=False;
+    with append=True the step's new tokens are stored and attended by one
+    pa_decode_attention_append call."""
     DeviceWorkload = _device()
     _say(f"[case] {wl.name} partition={partition} vector_only={vector_only} "
-         f"fused_write={fused_write}")
+         f"fused_write={fused_write} append={append}")
     dev = DeviceWorkload(wl)
+    if append:
+        assert dev.step_uses_append()
     dev.run_setup(fused_write=fused_write)
     out = dev.run_step(partition_size=partition, vector_only=vector_only,
-                       fused_write=fused_write).cpu().numpy()
+                       fused_write=fused_write, append=append).cpu().numpy()
     torch.cuda.synchronize()
     kp, vp, ref, slots_ref = run_oracle(wl, wl.setup + wl.step, seqs=seqs, heads=heads)
     got_slots = dev.slots_of(dev.setup_ops + dev.step_ops)
@@ -69,6 +73,35 @@ def test_workload_parity_small(cid):
     err = max_abs_err(out, ref)
     _say(f"  max_abs_err={err:.3e}")
     assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_append_parity(cid):
+    """pa_decode_attention_append: the new tokens land in their slots (pools
+    bit-exact) and the output matches the oracle; on the stream-K path the
+    decode kernel itself reads and stores them."""
+    wl = W.make(cid, small=(cid != 1))
+    out, ref = run_both(wl, append=True)
+    assert max_abs_err(out, ref) <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+@pytest.mark.parametrize("partition", [None, 64])
+def test_append_equals_write_then_decode_bitwise(cid, partition):
+    """Appending inside the decode call changes where the new rows come from,
+    not the arithmetic: outputs and pools equal the two-call result bit for
+    bit, on the stream-K path and on fixed partitions."""
+    wl = W.make(cid, small=True)
+    DeviceWorkload = _device()
+    res = []
+    for append in (False, True):
+        dev = DeviceWorkload(wl)
+        dev.run_setup()
+        o = dev.run_step(partition_size=partition, append=append).cpu().numpy()
+        res.append((o, dev.pool_bits()))
+    assert res[0][0].tobytes() == res[1][0].tobytes()
+    assert res[0][1][0].tobytes() == res[1][1][0].tobytes()
+    assert res[0][1][1].tobytes() == res[1][1][1].tobytes()
 
 
 @pytest.mark.parametrize("cid", [1, 4])
@@ -126,10 +159,11 @@ def test_edge_shapes(shape):
     rng = np.random.default_rng(abs(hash(shape)) % (2**31))
     wl = W.decode_workload(f"edge {shape}", dtype, EDGE_CTX, hq, hkv, d, bs, rng=rng,
                            seed=(7, hq, hkv, d, bs))
-    for part in (None, max(16, bs), 4 * max(16, bs)):
-        out, ref = run_both(wl, partition=part, check_pools=(part is None))
+    for part, append in ((None, False), (max(16, bs), False), (4 * max(16, bs), False),
+                         (None, True)):
+        out, ref = run_both(wl, partition=part, check_pools=(part is None), append=append)
         err = max_abs_err(out, ref)
-        _say(f"  partition={part} max_abs_err={err:.3e}")
+        _say(f"  partition={part} append={append} max_abs_err={err:.3e}")
         assert err <= TOL[dtype]
         assert np.all(out[0] == 0.0)           # ctx == 0 gives zeros
         assert np.isfinite(out).all()

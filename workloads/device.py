@@ -50,6 +50,7 @@ class DeviceWorkload:
         self._ensure_workspace(wl.partition_size, False)
         self.setup_ops = [self._upload(op) for op in wl.setup]
         self.step_ops = [self._upload(op) for op in wl.step]
+        self.step_ops_append = self._fuse_append(wl.step, self.step_ops)
 
     def _upload(self, op):
         kind, x = op
@@ -67,6 +68,36 @@ class DeviceWorkload:
             return ("decode", x)
         raise ValueError(kind)
 
+    def _fuse_append(self, plan, ops):
+        """The step with each [write of one new token per non-empty sequence
+        at position ctx-1, decode on the same table] pair replaced by one
+        pa_decode_attention_append call (the new rows gathered into
+        [S][Hkv][D] arrays)."""
+        wl = self.wl
+        out = []
+        i = 0
+        while i < len(ops):
+            if (i + 1 < len(ops) and plan[i][0] == "write" and plan[i + 1][0] == "decode"
+                    and plan[i][1].table == plan[i + 1][1]):
+                x = plan[i][1]
+                ctx = wl.context_lens
+                nonempty = np.nonzero(ctx > 0)[0]
+                if (np.array_equal(np.sort(x.seq_ids), nonempty)
+                        and np.array_equal(x.positions, ctx[x.seq_ids] - 1)):
+                    kf = np.zeros((wl.num_seqs,) + x.k.shape[1:], dtype=x.k.dtype)
+                    vf = np.zeros_like(kf)
+                    kf[x.seq_ids] = x.k
+                    vf[x.seq_ids] = x.v
+                    out.append(("decode_append", dict(
+                        table=x.table, write=ops[i][1],
+                        k=to_device(kf, wl.dtype, self.device),
+                        v=to_device(vf, wl.dtype, self.device))))
+                    i += 2
+                    continue
+            out.append(ops[i])
+            i += 1
+        return out
+
     def _ensure_workspace(self, partition_size, vector_only):
         wl = self.wl
         need = pa.decode_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
@@ -78,14 +109,28 @@ class DeviceWorkload:
 
     # -------------------------------------------------------------------
     def _run(self, ops, pool=0, partition_size=None, vector_only=False, stream=None,
-             fused_write=True):
+             fused_write=True, record_slots=True):
         """Run `ops`.  A write is one pa_write_kv_at launch (slots computed and
         stored in the same kernel) or, with fused_write=False, pa_compute_slots
-        followed by pa_write_kv."""
+        followed by pa_write_kv.  A decode_append op is one
+        pa_decode_attention_append call; with record_slots its write's slots
+        are also computed (pa_compute_slots) for checking."""
         wl = self.wl
         k, v = self.pools[pool]
         part = wl.partition_size if partition_size is None else partition_size
         for kind, x in ops:
+            if kind == "decode_append":
+                w = x["write"]
+                if record_slots:
+                    pa.compute_slots(self.tables[x["table"]], w["positions"], wl.block_size,
+                                     wl.num_blocks, seq_ids=w["seq_ids"], out=w["slots"],
+                                     stream=stream)
+                ws = self._ensure_workspace(part, vector_only)
+                pa.decode_attention(self.q, k, v, self.tables[x["table"]], self.ctx, wl.scale,
+                                    self.max_ctx, partition_size=part, workspace=ws, out=self.out,
+                                    vector_only=vector_only, stream=stream, k_new=x["k"],
+                                    v_new=x["v"])
+                continue
             if kind == "write" and fused_write:
                 pa.write_kv_at(k, v, x["k"], x["v"], self.tables[x["table"]], x["positions"],
                                seq_ids=x["seq_ids"], slots_out=x["slots"], stream=stream)
@@ -106,8 +151,10 @@ class DeviceWorkload:
     def run_setup(self, pool=0, **kw):
         self._run(self.setup_ops, pool, **kw)
 
-    def run_step(self, pool=0, **kw):
-        return self._run(self.step_ops, pool, **kw)
+    def run_step(self, pool=0, append=False, **kw):
+        """The step's ops; with append=True the write of the new tokens and
+        the decode run as one pa_decode_attention_append call."""
+        return self._run(self.step_ops_append if append else self.step_ops, pool, **kw)
 
     def decode_only(self, pool=0, **kw):
         return self._run([op for op in self.step_ops if op[0] == "decode"], pool, **kw)
@@ -126,6 +173,9 @@ class DeviceWorkload:
 
     def slots_of(self, ops):
         return [x["slots"].cpu().numpy() for kind, x in ops if kind == "write"]
+
+    def step_uses_append(self):
+        return any(kind == "decode_append" for kind, _ in self.step_ops_append)
 
     def pool_bits(self, pool=0):
         k, v = self.pools[pool]
