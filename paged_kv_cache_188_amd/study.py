@@ -1,0 +1,104 @@
+"""Paging overhead and block size, measured with the decode kernels.
+
+[nalar] "Sisa alokasi tetap ada, tetapi dibatasi ukuran blok" trades tail
+waste (the unused slots of each sequence's last block) against metadata
+(table entries) as the block size changes, and [nalar] "Kernel attention
+harus mengikuti block table" notes that walking the table costs something.
+This study puts numbers on both with the library's own kernels: the
+Llama-3-8B-shaped decode batch (64 sequences, 32 query / 8 KV heads,
+head_dim 128, bf16, contexts uniform in [128, 4096]) at block sizes 8, 16,
+32 and 64, with blocks scattered through the pool (seeded shuffle) or
+contiguous per sequence (identity placement).  For each case it reports the
+decode call's time (HIP events, median), KV and algorithmic bandwidth, the
+fraction of allocated slots left unused, and the table bytes the kernel
+reads.  Same context lengths and contents in every case.
+
+    python -m paged_kv_cache_188_amd.study [--reps 30]
+
+prints one JSON line per case and a markdown table.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--reps", type=int, default=30)
+    args = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_188_amd as pa
+    import workloads as W
+    from workloads.device import DeviceWorkload
+
+    if not torch.cuda.is_available():
+        print("the study needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rng0 = np.random.default_rng(np.random.SeedSequence([188, 2]))
+    ctx = rng0.integers(128, 4096, size=64, endpoint=True).astype(np.int32)
+    rows = []
+    for bs in (8, 16, 32, 64):
+        for shuffle in (True, False):
+            rng = np.random.default_rng(np.random.SeedSequence([188, 2, bs, int(shuffle)]))
+            wl = W.decode_workload(f"llama3-8b-decode bs={bs} {'shuffled' if shuffle else 'contiguous'}",
+                                   W.BF16, ctx, 32, 8, 128, bs, rng=rng, seed=(188, 2),
+                                   max_blocks_per_seq=math.ceil(4096 / bs), shuffle=shuffle)
+            dev = DeviceWorkload(wl)
+            dev.run_setup()
+            dev.release_setup_inputs()
+            pool_bytes = 2 * dev.pools[0][0].numel() * dev.pools[0][0].element_size()
+            npools = max(2, min(8, -(-(1 << 30) // pool_bytes) + 1))
+            dev.add_pool_copies(npools - 1)
+            ops = dev.step_ops_append
+            for k in range(5):
+                dev._run(ops, k % npools, record_slots=False)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.reps)]
+            stream = torch.cuda.current_stream()
+            for k, (a, b) in enumerate(ev):
+                a.record(stream)
+                dev._run(ops, k % npools, record_slots=False)
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in ev)
+            med = ms[len(ms) // 2]
+            blocks = np.ceil(ctx / bs).astype(np.int64)
+            allocated = int((blocks * bs).sum())
+            workers = pa.decode_streamk_workers(wl.num_seqs, wl.head_dim, bs, 0, dev.torch_dtype)
+            row = {
+                "block_size": bs, "placement": "shuffled" if shuffle else "contiguous",
+                "decode_call_us": round(med * 1e3, 2),
+                "kv_GBps": round(wl.kv_bytes_read() / med / 1e6, 1),
+                "algorithmic_GBps": round(wl.decode_bytes() / med / 1e6, 1),
+                "frac_of_8TBps": round(wl.decode_bytes() / med / 1e6 / 8000.0, 4),
+                "path": "stream-K" if workers > 0 else "fixed partitions",
+                "tail_waste_frac": round(1 - int(ctx.sum()) / allocated, 5),
+                "table_bytes_read": int(4 * blocks.sum()),
+            }
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+            del dev
+            torch.cuda.empty_cache()
+    print("| block size | placement | decode call (us) | KV GB/s | frac of 8 TB/s | path | "
+          "unused slots | table bytes |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['block_size']} | {r['placement']} | {r['decode_call_us']} | {r['kv_GBps']} | "
+              f"{r['frac_of_8TBps']} | {r['path']} | {100 * r['tail_waste_frac']:.2f} % | "
+              f"{r['table_bytes_read']} |")
+
+
+if __name__ == "__main__":
+    main()

@@ -214,11 +214,12 @@ def _history_kv(seed, stream_id, n_tokens, num_kv_heads, head_dim, dtype):
 def decode_workload(name, dtype, ctx_lens, num_q_heads, num_kv_heads, head_dim,
                     block_size, *, rng, seed=(), pool_slack=1.1, num_blocks=None,
                     max_blocks_per_seq=None, partition_size=0, scale=None,
-                    table_prefix_only=False):
+                    table_prefix_only=False, shuffle=True):
     """One new token per sequence at position ``ctx-1``; history ``0..ctx-2``
     is written in setup.  Physical blocks come from a seeded permutation of the
-    pool, taken in (sequence, logical block) order.  ``ctx == 0`` sequences get
-    no token and no block."""
+    pool (``shuffle=False``: the identity, i.e. every sequence's blocks
+    contiguous), taken in (sequence, logical block) order.  ``ctx == 0``
+    sequences get no token and no block."""
     ctx = np.asarray(ctx_lens, dtype=np.int32)
     S = ctx.size
     if not seed:
@@ -230,7 +231,7 @@ def decode_workload(name, dtype, ctx_lens, num_q_heads, num_kv_heads, head_dim,
     if num_blocks < need:
         raise ValueError("pool smaller than the blocks needed")
     mb = max_blocks_per_seq or (max(1, int(need_each.max())) if S else 1)
-    perm = rng.permutation(num_blocks).astype(np.int32)
+    perm = (rng.permutation(num_blocks) if shuffle else np.arange(num_blocks)).astype(np.int32)
     bt = np.full((S, mb), -1, dtype=np.int32)
     cursor = 0
     for i in range(S):
