@@ -86,7 +86,8 @@ typedef enum pa_status {
   PA_ERR_DTYPE = 3,        /* unknown element type                           */
   PA_ERR_UNSUPPORTED = 4,  /* head_dim, block_size or partition not supported*/
   PA_ERR_WORKSPACE = 5,    /* decode workspace missing or too small          */
-  PA_ERR_HIP = 6           /* the HIP runtime reported an error              */
+  PA_ERR_HIP = 6,          /* the HIP runtime reported an error              */
+  PA_ERR_CAPACITY = 7      /* block manager: no free block / sequence slot   */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;

@@ -25,14 +25,33 @@ PA_BF16 = 1
 PA_DECODE_VECTOR_ONLY = 1
 
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
-          4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
+          4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CAPACITY"}
 
-# name -> (restype, argtypes); mirrors include/pa.h
+# name -> (restype, argtypes); mirrors include/pa.h and include/pa_block_manager.h
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
+
+
+class BMStats(ctypes.Structure):
+    """pa_bm_stats (include/pa_block_manager.h)."""
+    _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
+                ("live_sequences", ctypes.c_int32), ("logical_blocks", ctypes.c_int64),
+                ("logical_tokens", ctypes.c_int64), ("stored_tokens", ctypes.c_int64),
+                ("physical_slots", ctypes.c_int64)]
+
+
 SIGNATURES = {
     "pa_abi_version": (_I32, []),
+    "pa_bm_create": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_void_p)]),
+    "pa_bm_destroy": (None, [_P]),
+    "pa_bm_add_sequence": (ctypes.c_int, [_P, _P]),
+    "pa_bm_fork": (ctypes.c_int, [_P, _I32, _P]),
+    "pa_bm_free_sequence": (ctypes.c_int, [_P, _I32]),
+    "pa_bm_append": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P]),
+    "pa_bm_tables": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
+    "pa_bm_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(BMStats)]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_compute_slots": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P]),
     "pa_write_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
@@ -281,3 +300,74 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max
         workspace.numel() if workspace is not None else 0, _dtype_code(k_cache),
         PA_DECODE_VECTOR_ONLY if vector_only else 0, _stream(stream)))
     return out
+
+
+class BlockManager:
+    """Host block manager of include/pa_block_manager.h (numpy in and out).
+
+    Hands out physical block ids of a pool of ``num_blocks`` blocks, keeps the
+    block tables, reference counts and copy-on-write; its slots, copy pairs
+    and tables feed write_kv, copy_blocks and decode_attention."""
+
+    def __init__(self, num_blocks, block_size, max_seqs, max_blocks_per_seq):
+        self.block_size = block_size
+        self.max_blocks_per_seq = max_blocks_per_seq
+        h = ctypes.c_void_p()
+        _check("pa_bm_create", lib().pa_bm_create(num_blocks, block_size, max_seqs,
+                                                  max_blocks_per_seq, ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+    def add_sequence(self):
+        out = ctypes.c_int32()
+        _check("pa_bm_add_sequence", lib().pa_bm_add_sequence(self._h, ctypes.byref(out)))
+        return out.value
+
+    def fork(self, parent):
+        out = ctypes.c_int32()
+        _check("pa_bm_fork", lib().pa_bm_fork(self._h, int(parent), ctypes.byref(out)))
+        return out.value
+
+    def free_sequence(self, seq):
+        _check("pa_bm_free_sequence", lib().pa_bm_free_sequence(self._h, int(seq)))
+
+    def append(self, seq_ids, counts):
+        """Slots (int64, all new tokens in order) and copy-on-write pairs
+        (int32 [k][2]) for counts[i] new tokens of seq_ids[i]."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        cnt = np.ascontiguousarray(counts, dtype=np.int32)
+        if ids.shape != cnt.shape or ids.ndim != 1:
+            raise ValueError("seq_ids and counts must be 1-D of one length")
+        slots = np.empty(int(cnt.sum()) if cnt.size else 0, dtype=np.int64)
+        pairs = np.empty((max(1, ids.size), 2), dtype=np.int32)
+        ncopy = ctypes.c_int32()
+        _check("pa_bm_append", lib().pa_bm_append(
+            self._h, ids.ctypes.data, cnt.ctypes.data, ids.size, slots.ctypes.data,
+            pairs.ctypes.data, ctypes.byref(ncopy)))
+        return slots, pairs[:ncopy.value].copy()
+
+    def tables(self, seq_ids):
+        """(tables int32 [n][max_blocks_per_seq] padded with -1, lengths int32 [n])."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        t = np.empty((ids.size, self.max_blocks_per_seq), dtype=np.int32)
+        lens = np.empty(ids.size, dtype=np.int32)
+        _check("pa_bm_tables", lib().pa_bm_tables(self._h, ids.ctypes.data, ids.size,
+                                                  t.ctypes.data, lens.ctypes.data))
+        return t, lens
+
+    def stats(self):
+        st = BMStats()
+        _check("pa_bm_get_stats", lib().pa_bm_get_stats(self._h, ctypes.byref(st)))
+        return {name: getattr(st, name) for name, _ in BMStats._fields_}

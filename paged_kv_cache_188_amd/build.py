@@ -2,7 +2,7 @@
 
     python -m paged_kv_cache_188_amd.build
 
-Every HIP source under csrc/ is compiled to an object in parallel, then linked
+Every source under csrc/ (HIP and host C++) is compiled to an object in parallel, then linked
 into paged_kv_cache_188_amd/libpa.so.  The library is replaced atomically, so
 a process that already loaded the previous build keeps a consistent copy.
 """
@@ -38,7 +38,8 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    """HIP kernels and launchers (*.hip) and host-only C++ (*.cpp)."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src: str, verbose: bool) -> str:

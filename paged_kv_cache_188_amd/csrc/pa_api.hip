@@ -89,6 +89,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "head_dim, block_size, partition or alignment not supported";
     case PA_ERR_WORKSPACE: return "decode workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_CAPACITY: return "no free block or sequence slot left";
   }
   return "unknown status";
 }
