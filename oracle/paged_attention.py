@@ -284,3 +284,71 @@ def decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
             w = np.exp(s - s.max())
             out[i, h] = (w @ v_t) / w.sum()
     return out
+
+
+# ---------------------------------------------------------------------------
+# multi-query attention of a prompt chunk (chunked prefill)
+# ---------------------------------------------------------------------------
+
+def prefill_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                      block_tables: np.ndarray, context_lens: np.ndarray,
+                      query_start: np.ndarray, scale: float, dtype: str) -> np.ndarray:
+    """Exact causal softmax attention of a chunk of query tokens per sequence,
+    float64.
+
+    [bicarait] "Blueprint Arsitektur 3: Chunked Prefill": a prompt is
+    processed a chunk (e.g. 512 tokens) at a time, interleaved with decode
+    steps; each chunk's tokens attend to everything before them through the
+    same block table as the decode ([nalar] "Kernel attention harus mengikuti
+    block table").  Reading (the page gives no formula): sequence i's chunk is
+    the last ``L = query_start[i+1] - query_start[i]`` of its ``n =
+    context_lens[i]`` tokens, already in the cache; chunk token j is logical
+    position ``n - L + j`` and, as in ordinary causal self-attention, sees
+    positions ``0 .. n - L + j``:
+
+        s_t   = scale * <q_{j,h}, K_t>          t = 0 .. n - L + j
+        out   = sum_t softmax(s)_t * V_t
+
+    A token whose position is negative (a chunk longer than its context) sees
+    no key and gets zeros, like an empty decode context.  q and the result are
+    ``[T][Hq][D]`` with T = query_start[-1]; head h reads KV head h // G.
+    """
+    total, num_q_heads, head_dim = q.shape
+    num_blocks, num_kv_heads, block_size, head_dim_kv, _ = pool_dims(k_pool, v_pool)
+    if head_dim_kv != head_dim or num_q_heads % num_kv_heads:
+        raise ContractError("q and the pools disagree")
+    group = num_q_heads // num_kv_heads
+    bt = np.asarray(block_tables)
+    ctx = np.asarray(context_lens)
+    qs = np.asarray(query_start, dtype=np.int64)
+    if qs.shape != (ctx.size + 1,) or qs[0] < 0 or np.any(np.diff(qs) < 0) or qs[-1] > total:
+        raise ContractError("query_start must be non-decreasing within the query rows")
+    scale64 = np.float64(np.float32(scale))
+    q64 = to_f64(q, dtype)
+    out = np.zeros((total, num_q_heads, head_dim), dtype=np.float64)
+    for i in range(ctx.size):
+        n, L = int(ctx[i]), int(qs[i + 1] - qs[i])
+        if n < 0 or n > bt.shape[1] * block_size:
+            raise ContractError(f"sequence {i}: context length {n} outside the table")
+        if L == 0 or n == 0:
+            continue
+        t = np.arange(n)
+        lb = np.array([_logical_block(int(p), block_size) for p in t])
+        off = np.array([_offset_in_block(int(p), block_size) for p in t])
+        phys = bt[i, lb]
+        if phys.min() < 0 or phys.max() >= num_blocks:
+            raise ContractError(f"sequence {i}: table entry is not a pool block")
+        pos = n - L + np.arange(L)                   # position of each chunk token
+        visible = t[None, :] <= pos[:, None]         # [L][n]: key t seen by token j
+        seen = visible.any(axis=1)                   # tokens at a position >= 0
+        for g in range(num_kv_heads):
+            k_t = to_f64(_k_rows(k_pool, phys, g, off), dtype)   # [n][D]
+            v_t = to_f64(v_pool[phys, g, off, :], dtype)         # [n][D]
+            for h in range(g * group, (g + 1) * group):
+                s = scale64 * (q64[qs[i]:qs[i + 1], h] @ k_t.T)  # [L][n]
+                s = np.where(visible, s, -np.inf)
+                top = np.where(seen, s.max(axis=1), 0.0)
+                w = np.where(visible, np.exp(s - top[:, None]), 0.0)
+                den = np.where(seen, w.sum(axis=1), 1.0)
+                out[qs[i]:qs[i + 1], h] = (w @ v_t) / den[:, None]
+    return out

@@ -430,6 +430,108 @@ def pin_cow_isolation(O):
     assert k3[4].tobytes() == kp[4].tobytes() and v3[4].tobytes() == vp[4].tobytes()
 
 
+# ---------------------------------------------------------------------------
+# multi-query attention of a prompt chunk (chunked prefill)
+# ---------------------------------------------------------------------------
+
+def prefill_case(rng, *, ctx, chunk, hq, hkv, d, bs, dtype, x=1, slack=3):
+    """random_case plus, for each sequence, a chunk of ``chunk[i]`` query
+    tokens (the last ones of its context) and their start offsets."""
+    c = random_case(rng, num_seqs=len(ctx), hq=hq, hkv=hkv, d=d, bs=bs, ctx_max=max(ctx),
+                    dtype=dtype, ctx=list(ctx), x=x, slack=slack)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    c["qs"] = qs
+    c["q"] = random_values(rng, (int(qs[-1]), hq, d), dtype)
+    return c
+
+
+def prefill_bruteforce(c, scale):
+    """Chunk token j of sequence i (position n - L + j) by the textbook loops
+    over its visible prefix K[0 .. n-L+j], one query at a time."""
+    qs, q = c["qs"], c["q"]
+    out = np.zeros(q.shape)
+    for i, n in enumerate(c["ctx"]):
+        L = int(qs[i + 1] - qs[i])
+        for j in range(L):
+            pos = int(n) - L + j
+            if pos < 0:
+                continue
+            row = q[qs[i] + j][None]
+            out[qs[i] + j] = dense_attention_loops(
+                row, [c["k_logical"][i][:pos + 1]], [c["v_logical"][i][:pos + 1]], scale,
+                c["dtype"])[0]
+    return out
+
+
+PREFILL_CASES = [  # (ctx, chunk, hq, hkv, d, bs, dtype, x, seed)
+    ([9, 5, 12], [4, 5, 3], 4, 2, 4, 4, "bf16", 2, 1),      # prefix + chunk, whole prompt
+    ([7, 16], [7, 1], 2, 1, 3, 2, "f32", 1, 2),            # L = 1 is a decode
+    ([3, 10], [5, 0], 6, 3, 2, 8, "f32", 2, 3),            # chunk longer than its context
+]
+
+
+def pin_prefill_bruteforce(O):
+    """Each chunk token equals textbook attention of its own query over the
+    keys up to its position ([bicarait] "Blueprint Arsitektur 3": a chunk
+    sees the whole prompt before it; causal inside the chunk)."""
+    for (ctx, chunk, hq, hkv, d, bs, dtype, x, seed) in PREFILL_CASES:
+        c = prefill_case(np.random.default_rng(300 + seed), ctx=ctx, chunk=chunk, hq=hq,
+                         hkv=hkv, d=d, bs=bs, dtype=dtype, x=x)
+        scale = float(np.float32(0.61))
+        got = O.prefill_attention(c["q"], c["kp"], c["vp"], c["tables"], c["ctx"], c["qs"],
+                                  scale, dtype)
+        want = prefill_bruteforce(c, scale)
+        assert np.max(np.abs(got - want), initial=0.0) <= 1e-12, (ctx, chunk)
+
+
+def pin_prefill_sdpa(O):
+    """A chunk's rows are the last L rows of ordinary causal self-attention
+    over the whole context (torch's float64 scaled_dot_product_attention with
+    is_causal, grouped heads expanded)."""
+    import torch
+    rng = np.random.default_rng(41)
+    for (n, L, hq, hkv, d, bs, x) in ((37, 37, 8, 2, 16, 8, 8), (50, 13, 4, 4, 8, 16, 4),
+                                      (24, 24, 6, 1, 4, 4, 1)):
+        c = prefill_case(rng, ctx=[n], chunk=[L], hq=hq, hkv=hkv, d=d, bs=bs, dtype="bf16", x=x)
+        scale = float(np.float32(0.29))
+        got = O.prefill_attention(c["q"], c["kp"], c["vp"], c["tables"], c["ctx"], c["qs"],
+                                  scale, "bf16")
+        conv = np.vectorize(bf16_bits_to_float)
+        # queries: positions 0 .. n-L-1 are zero rows (not compared), then the chunk
+        qf = np.zeros((n, hq, d))
+        qf[n - L:] = conv(c["q"])
+        q = torch.tensor(qf).permute(1, 0, 2).unsqueeze(0).contiguous()
+        k = torch.tensor(conv(c["k_logical"][0])).permute(1, 0, 2)
+        v = torch.tensor(conv(c["v_logical"][0])).permute(1, 0, 2)
+        k = k.repeat_interleave(hq // hkv, dim=0).unsqueeze(0).contiguous()
+        v = v.repeat_interleave(hq // hkv, dim=0).unsqueeze(0).contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True,
+                                                               scale=scale)
+        ref = ref[0].permute(1, 0, 2).numpy()[n - L:]
+        assert np.max(np.abs(got - ref)) <= 1e-12, np.max(np.abs(got - ref))
+
+
+def pin_prefill_chunks_compose(O):
+    """Chunking changes nothing: a prompt attended in three chunks (each with
+    the context it has at that point) gives the rows of the one-chunk run;
+    and L = 1 gives the decode result."""
+    rng = np.random.default_rng(43)
+    n, hq, hkv, d, bs = 29, 4, 2, 4, 4
+    c = prefill_case(rng, ctx=[n], chunk=[n], hq=hq, hkv=hkv, d=d, bs=bs, dtype="f32", x=2)
+    whole = O.prefill_attention(c["q"], c["kp"], c["vp"], c["tables"], c["ctx"], c["qs"], 0.5,
+                                "f32")
+    for a, b in ((0, 11), (11, 12), (12, 29)):
+        part = O.prefill_attention(c["q"][a:b], c["kp"], c["vp"], c["tables"],
+                                   np.array([b], np.int32), np.array([0, b - a], np.int32), 0.5,
+                                   "f32")
+        assert np.max(np.abs(part - whole[a:b])) <= 1e-13
+    for pos in (0, 5, 28):
+        dec = O.decode_attention(c["q"][pos][None], c["kp"], c["vp"], c["tables"],
+                                 np.array([pos + 1], np.int32), 0.5, "f32")
+        assert np.max(np.abs(dec[0] - whole[pos])) <= 1e-13
+
+
 ALL_PINS = [pin_value_decoding, pin_worked_tables, pin_slot_bijection, pin_write_bruteforce,
             pin_write_roundtrip, pin_copy, pin_attention_dense, pin_attention_sdpa,
-            pin_closed_forms, pin_shared_vs_private, pin_cow_isolation]
+            pin_closed_forms, pin_shared_vs_private, pin_cow_isolation, pin_prefill_bruteforce,
+            pin_prefill_sdpa, pin_prefill_chunks_compose]
