@@ -11,6 +11,8 @@
  *   pa_decode_attention  one query token per sequence attends to its history,
  *                        reached block by block through its block table
  *   pa_decode_attention_append  the new tokens stored and attended in one call
+ *   pa_prefill_attention  several query tokens per sequence (a prompt chunk),
+ *                        causal, over the same pools
  *
  * Sources, cited by page title and section:
  *   [nalar]    "PagedAttention: memetakan blok KV logis ke memori fisik tidak
@@ -282,6 +284,40 @@ pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache,
                                      uint32_t flags, void* stream);
 
 /* Text of a status code (static storage). */
+/* ---------------------------------------------------------------------------
+ * pa_prefill_attention  (multi-query paged attention: a prompt chunk)
+ *
+ * The prefill side of [bicarait] "Blueprint Arsitektur 3: Chunked Prefill":
+ * a long prompt is processed a chunk at a time, every chunk attending to the
+ * cache through the same block tables as the decode.  Sequence i has L_i =
+ * query_start[i+1] - query_start[i] query tokens, rows query_start[i] ..
+ * query_start[i+1]-1 of q and out; its context n_i = context_lens[i]
+ * (clamped to [0, max_blocks_per_seq * block_size]) counts the chunk, whose
+ * K/V must already be in the cache (pa_write_kv).  Query token j sits at
+ * position n_i - L_i + j and attends causally to positions 0 .. n_i - L_i + j
+ * (softmax attention as pa_decode_attention, grouped-query heads likewise);
+ * a token at a negative position (L_i > n_i) sees nothing and gets zeros.
+ * L_i = 1 is exactly the decode.
+ *   q      [num_q_tokens][num_q_heads][head_dim] bf16
+ *   out    [num_q_tokens][num_q_heads][head_dim] float32
+ *   query_start [num_seqs + 1] int32, non-decreasing, query_start[0] >= 0,
+ *          query_start[num_seqs] <= num_q_tokens (device memory).  Rows of a
+ *          sequence that breaks this are not written; neither are rows of
+ *          tokens j >= max_query_len (pass max_query_len >= every L_i).
+ * bf16 only, block_size >= 16, num_q_heads / num_kv_heads <= 16, head_dim
+ * 64 or 128 (else PA_ERR_UNSUPPORTED).  No workspace; deterministic.
+ * ------------------------------------------------------------------------- */
+pa_status pa_prefill_attention(float* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens,
+                               const int32_t* query_start, int32_t num_seqs,
+                               int32_t num_q_tokens, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq,
+                               int32_t max_query_len, float scale,
+                               pa_dtype dtype, void* stream);
+
 const char* pa_status_string(pa_status status);
 
 /* PA_ABI_VERSION of the built library. */

@@ -70,6 +70,9 @@ SIGNATURES = {
                                                   _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                   ctypes.c_float, _I32, _P, ctypes.c_size_t,
                                                   ctypes.c_int, ctypes.c_uint32, _P]),
+    "pa_prefill_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                            _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
+                                            ctypes.c_int, _P]),
 }
 
 
@@ -299,6 +302,34 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max
         int(partition_size), _ptr(workspace) if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _dtype_code(k_cache),
         PA_DECODE_VECTOR_ONLY if vector_only else 0, _stream(stream)))
+    return out
+
+
+def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                      max_query_len, out=None, stream=None):
+    """Multi-query (chunked prefill) paged attention, bf16; returns float32
+    [T][Hq][D] for q [T][Hq][D].  Sequence i owns rows query_start[i] ..
+    query_start[i+1]-1 (int32 [S+1]); its chunk ends its context
+    context_lens[i] and attends causally (pa_prefill_attention)."""
+    import torch
+    t, hq, d = q.shape
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
+    if d2 != d:
+        raise ValueError("q and the pools disagree in head_dim")
+    _need(q, k_cache.dtype, "q")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    _need(query_start, torch.int32, "query_start")
+    s = context_lens.shape[0]
+    if query_start.shape != (s + 1,) or block_tables.shape[0] != s:
+        raise ValueError("query_start must be [S+1] and block_tables [S][MB]")
+    if out is None:
+        out = torch.empty((t, hq, d), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    _check("pa_prefill_attention", lib().pa_prefill_attention(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), s, t, hq, hkv, d, bs, nb, block_tables.shape[1],
+        int(max_query_len), float(scale), _dtype_code(k_cache), _stream(stream)))
     return out
 
 

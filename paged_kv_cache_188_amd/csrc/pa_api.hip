@@ -240,7 +240,11 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
                                       : choose_partition(num_seqs, num_kv_heads, block_size,
                                                          max_context_len);
   const int64_t P = max_context_len > 0 ? (max_context_len + (int64_t)part - 1) / part : 1;
-  if ((int64_t)num_seqs * num_kv_heads * P / 4 >= INT32_MAX) return PA_ERR_SHAPE;
+  // a launch holds at most 2^32 - 1 work-items: on the fixed-partition path
+  // one wave per work item and 256 threads per (sequence, head) in the merge
+  if (path != pa::DecodePath::kStreamK && ((int64_t)num_seqs * num_kv_heads * P * 64 > UINT32_MAX ||
+                                           (int64_t)num_seqs * num_q_heads * 256 > UINT32_MAX))
+    return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   const pa::DecodeWorkspace ws =
       path == pa::DecodePath::kStreamK
@@ -341,6 +345,53 @@ pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache, v
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
                      workspace, workspace_bytes, dtype, flags, true, stream);
+}
+
+pa_status pa_prefill_attention(float* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start,
+                               int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_query_len, float scale, pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_tokens < 0 || max_query_len < 0 || num_q_heads < 1 ||
+      num_kv_heads < 1 || num_blocks < 1 || max_blocks_per_seq < 1 ||
+      num_q_heads % num_kv_heads)
+    return PA_ERR_SHAPE;
+  if (dtype != PA_BF16 || block_size < 16) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  {  // one wave per (sequence, KV head, 16 / G query tokens); <= 2^32 - 1 work-items
+    const int32_t tq = 16 / (num_q_heads / num_kv_heads);
+    if ((int64_t)num_seqs * num_kv_heads * ((max_query_len + tq - 1) / tq) * 64 > UINT32_MAX)
+      return PA_ERR_SHAPE;
+  }
+  if (num_seqs == 0 || num_q_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  pa::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.block_size = block_size;
+  p.max_tokens = max_blocks_per_seq * block_size;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(pa::launch_prefill(p, query_start, num_q_tokens, max_query_len, head_dim,
+                                     block_size, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -94,6 +94,10 @@ DecodePath decode_path(int num_seqs, int block_size, pa_dtype dtype, int partiti
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, pa_dtype dtype,
                          bool vector_only, DecodePath path, hipStream_t stream);
 
+// Multi-query (chunked prefill) attention, bf16, block_size >= 16.
+hipError_t launch_prefill(const DecodeParams& p, const int32_t* query_start, int64_t total_q,
+                          int max_query_len, int head_dim, int block_size, hipStream_t stream);
+
 // Workspace offsets (bytes); shared by the size query and the launch.
 struct DecodeWorkspace {
   size_t m_off, l_off, acc_off, handoff_off, total;

@@ -21,6 +21,9 @@ def run_oracle(wl, ops, kp=None, vp=None, seqs=None, heads=None):
             kp, vp = O.write_kv(kp, vp, x.k, x.v, s)
         elif kind == "copy":
             kp, vp = O.copy_blocks(kp, vp, x)
+        elif kind == "prefill":
+            out = O.prefill_attention(wl.q, kp, vp, wl.tables[x], wl.context_lens,
+                                      wl.query_start, wl.scale, wl.dtype)
         else:
             out = O.decode_attention(wl.q, kp, vp, wl.tables[x], wl.context_lens, wl.scale,
                                      wl.dtype, seqs=seqs, heads=heads)

@@ -112,6 +112,38 @@ def test_decode_validation(lib):
     assert ap(out=NULL) == NUL
 
 
+def _prefill(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, ctx=FAKE, qs=FAKE, S=2, T=64, Hq=8,
+             Hkv=2, D=128, bs=16, NB=10, MB=4, max_q=40, scale=0.1, dtype=1)
+    a.update(kw)
+    return lib.pa_prefill_attention(a["out"], a["q"], a["k"], a["v"], a["bt"], a["ctx"], a["qs"],
+                                    a["S"], a["T"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"],
+                                    a["MB"], a["max_q"], a["scale"], a["dtype"], NULL)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, dtype=7) == DTYPE
+    assert _prefill(lib, dtype=0) == UNSUP                 # float32: bf16 only
+    assert _prefill(lib, bs=8) == UNSUP                    # tiles need 16-token blocks
+    assert _prefill(lib, Hq=34, Hkv=2) == UNSUP            # group of 17
+    assert _prefill(lib, Hq=6, Hkv=4) == SHAPE
+    assert _prefill(lib, D=96) == UNSUP
+    assert _prefill(lib, S=-1) == SHAPE
+    assert _prefill(lib, T=-1) == SHAPE
+    assert _prefill(lib, max_q=-1) == SHAPE
+    assert _prefill(lib, NB=0) == SHAPE
+    assert _prefill(lib, scale=float("inf")) == SHAPE
+    assert _prefill(lib, qs=NULL) == NUL
+    assert _prefill(lib, out=NULL) == NUL
+    assert _prefill(lib, q=MISALIGNED) == UNSUP
+    # more than 2^32 work-items in one launch
+    assert _prefill(lib, S=1 << 20, Hkv=8, Hq=32, max_q=1 << 10) == SHAPE
+    # nothing to do: no HIP call
+    assert _prefill(lib, S=0, out=NULL) == OK
+    assert _prefill(lib, T=0, out=NULL) == OK
+    assert _prefill(lib, max_q=0, out=NULL) == OK
+
+
 def test_workspace_and_partition_rules(lib):
     # the library's partition choice (see pa_api.hip): 8B-shaped decode -> 512
     assert pa.decode_partition_size(64, 8, 16, 4096) == 512

@@ -107,6 +107,9 @@ class Workload:
     partition_size: int = 0            # 0: the library picks
     seed: tuple = ()
     notes: dict = field(default_factory=dict)
+    # multi-query (chunked prefill) workloads: sequence i owns query rows
+    # query_start[i] .. query_start[i+1]-1 of q ([T][Hq][D])
+    query_start: np.ndarray = None
 
     @property
     def group(self) -> int:
@@ -138,6 +141,26 @@ class Workload:
         return (self.kv_bytes_read()
                 + self.num_seqs * self.num_q_heads * self.head_dim * (e + 4)
                 + 4 * blocks + 4 * self.num_seqs)
+
+    # --- accounting of a chunked-prefill step ------------------------------
+    @property
+    def max_query_len(self) -> int:
+        return int(np.diff(self.query_start).max()) if self.num_seqs else 0
+
+    def prefill_flops(self) -> int:
+        """Multiply-adds x 2 of QK^T and PV over the keys each chunk token
+        sees (positions 0 .. its own): the causal work, nothing masked."""
+        qs, ctx = self.query_start.astype(np.int64), self.context_lens.astype(np.int64)
+        L = np.diff(qs)
+        # sum over j < L of (n - L + j + 1) keys
+        keys = int((L * (ctx - L) + L * (L + 1) // 2).sum())
+        return 4 * keys * self.num_q_heads * self.head_dim
+
+    def prefill_bytes(self) -> int:
+        """Each context token's K and V once per KV head, Q in, fp32 out."""
+        e = elem_bytes(self.dtype)
+        t = int(self.query_start[-1])
+        return (self.kv_bytes_read() + t * self.num_q_heads * self.head_dim * (e + 4))
 
     def unique_kv_bytes(self) -> int:
         """KV bytes of distinct physical blocks referenced by the final tables."""
@@ -258,6 +281,77 @@ def decode_workload(name, dtype, ctx_lens, num_q_heads, num_kv_heads, head_dim,
     wl.step.append(("write", Write("final", new_seq, new_pos, nk, nv)))
     wl.step.append(("decode", "final"))
     return wl
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill: a chunk of query tokens per sequence
+# ---------------------------------------------------------------------------
+
+def prefill_workload(name, dtype, prefix_lens, chunk_lens, num_q_heads, num_kv_heads, head_dim,
+                     block_size, *, rng, seed=(), pool_slack=1.1, shuffle=True):
+    """Sequence i has ``prefix_lens[i]`` tokens in the cache (written in
+    setup) and a chunk of ``chunk_lens[i]`` new prompt tokens at positions
+    prefix .. prefix+chunk-1: the step writes their K/V and runs the
+    multi-query attention of the chunk (context = prefix + chunk).  Blocks
+    are drawn as in decode_workload.  Draw order: block permutation -> Q ->
+    chunk K -> chunk V; the prefix K/V come from _history_kv."""
+    pre = np.asarray(prefix_lens, dtype=np.int32)
+    L = np.asarray(chunk_lens, dtype=np.int32)
+    ctx = (pre + L).astype(np.int32)
+    S = ctx.size
+    if not seed:
+        seed = tuple(int(x) for x in rng.integers(0, 2**31 - 1, size=2))
+    need_each = np.array([_blocks_for(int(c), block_size) for c in ctx], dtype=np.int64)
+    need = int(need_each.sum())
+    num_blocks = max(1, math.ceil(pool_slack * need))
+    mb = max(1, int(need_each.max())) if S else 1
+    perm = (rng.permutation(num_blocks) if shuffle else np.arange(num_blocks)).astype(np.int32)
+    bt = np.full((S, mb), -1, dtype=np.int32)
+    cursor = 0
+    for i in range(S):
+        n = int(need_each[i])
+        bt[i, :n] = perm[cursor:cursor + n]
+        cursor += n
+    qs = np.concatenate([[0], np.cumsum(L, dtype=np.int64)]).astype(np.int32)
+    q = draw_normal(rng, (int(qs[-1]), num_q_heads, head_dim), dtype)
+    hk, hv = _history_kv(seed, 1, int(pre.astype(np.int64).sum()), num_kv_heads, head_dim, dtype)
+    hs, hp = _positions(pre)
+    cs, cp = _positions(L, starts=pre)
+    ck = draw_normal(rng, (cs.size, num_kv_heads, head_dim), dtype)
+    cv = draw_normal(rng, (cs.size, num_kv_heads, head_dim), dtype)
+    wl = Workload(name=name, dtype=dtype, num_seqs=S, num_q_heads=num_q_heads,
+                  num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                  num_blocks=num_blocks, max_blocks_per_seq=mb,
+                  scale=float(np.float32(1.0 / math.sqrt(head_dim))), q=q,
+                  tables={"final": bt}, context_lens=ctx, seed=seed, query_start=qs)
+    wl.setup.append(("write", Write("final", hs, hp, hk, hv)))
+    wl.step.append(("write", Write("final", cs, cp, ck, cv)))
+    wl.step.append(("prefill", "final"))
+    return wl
+
+
+PREFILL_NAME = "chunked prefill Llama-3-8B-shape 16 seqs x 512-token chunks, prefix U[0,3584]"
+
+
+def make_prefill(small: bool = False, *, block_size: int = 16) -> Workload:
+    """The chunked-prefill workload: 512-token prompt chunks ([bicarait]
+    "Blueprint Arsitektur 3"), Llama-3-8B attention shape (32 query heads,
+    8 KV heads, head_dim 128), bf16, 16-token blocks.  16 sequences with a
+    prefix already cached (uniform in [0, 3584], so contexts reach 4096);
+    12 chunks are full 512-token chunks and 4 are a prompt's last, shorter
+    chunk (uniform in [1, 511]).  ``small``: 4 sequences, prefixes in
+    [0, 200], chunks of up to 70 tokens (several tiles, ragged tails)."""
+    rng, seed = _rng(600 if small else 60)
+    if small:
+        pre = rng.integers(0, 200, size=4, endpoint=True)
+        chunk = np.array([70, 33, 1, int(rng.integers(2, 70))])
+        name = PREFILL_NAME + " [small]"
+    else:
+        pre = rng.integers(0, 3584, size=16, endpoint=True)
+        chunk = np.full(16, 512)
+        chunk[12:] = rng.integers(1, 511, size=4, endpoint=True)
+        name = PREFILL_NAME
+    return prefill_workload(name, BF16, pre, chunk, 32, 8, 128, block_size, rng=rng, seed=seed)
 
 
 # ---------------------------------------------------------------------------

@@ -42,8 +42,11 @@ class DeviceWorkload:
         self.tables = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device)
                        for k, v in wl.tables.items()}
         self.ctx = torch.from_numpy(np.ascontiguousarray(wl.context_lens)).to(device)
-        self.out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32,
+        rows = wl.num_seqs if wl.query_start is None else int(wl.query_start[-1])
+        self.out = torch.empty((rows, wl.num_q_heads, wl.head_dim), dtype=torch.float32,
                                device=device)
+        self.qs = (None if wl.query_start is None else
+                   torch.from_numpy(np.ascontiguousarray(wl.query_start)).to(device))
         self.max_ctx = wl.max_context_len
         self.torch_dtype = torch.bfloat16 if wl.dtype == BF16 else torch.float32
         self.workspace = torch.empty(1, dtype=torch.uint8, device=device)
@@ -64,8 +67,8 @@ class DeviceWorkload:
                 slots=torch.empty(x.positions.size, dtype=torch.int64, device=self.device)))
         if kind == "copy":
             return ("copy", torch.from_numpy(np.ascontiguousarray(x)).to(self.device))
-        if kind == "decode":
-            return ("decode", x)
+        if kind in ("decode", "prefill"):
+            return (kind, x)
         raise ValueError(kind)
 
     def _fuse_append(self, plan, ops):
@@ -141,6 +144,9 @@ class DeviceWorkload:
                 pa.write_kv(k, v, x["k"], x["v"], x["slots"], stream=stream)
             elif kind == "copy":
                 pa.copy_blocks(k, v, x, stream=stream)
+            elif kind == "prefill":
+                pa.prefill_attention(self.q, k, v, self.tables[x], self.ctx, self.qs, wl.scale,
+                                     wl.max_query_len, out=self.out, stream=stream)
             else:
                 ws = self._ensure_workspace(part, vector_only)
                 pa.decode_attention(self.q, k, v, self.tables[x], self.ctx, wl.scale, self.max_ctx,
@@ -157,7 +163,9 @@ class DeviceWorkload:
         return self._run(self.step_ops_append if append else self.step_ops, pool, **kw)
 
     def decode_only(self, pool=0, **kw):
-        return self._run([op for op in self.step_ops if op[0] == "decode"], pool, **kw)
+        """The step's attention op(s) alone (decode or prefill)."""
+        return self._run([op for op in self.step_ops if op[0] in ("decode", "prefill")], pool,
+                         **kw)
 
     def release_setup_inputs(self):
         """Drop the uploaded history (only the setup ops need it)."""
