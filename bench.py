@@ -16,6 +16,12 @@ step is served from a cache warmed by the previous one.
 prints ONE JSON line: KV GB/s of the whole step (`value`), seq-steps/s,
 the decode kernel's roofline fraction (HIP events around every decode
 launch on the stream it runs on) and the CPU oracle's rate on a bounded sample.
+
+    python bench.py --workload prefill
+
+measures the chunked-prefill step instead (the chunk's K/V stored with
+pa_write_kv_at, then pa_prefill_attention): useful TFLOP/s of the causal
+attention against the bf16 matrix-core peak.
 """
 
 from __future__ import annotations
@@ -30,7 +36,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seq-steps/sec"
+PREFILL_METRIC = "chunked-prefill paged attention: useful TFLOP/s (causal, % of bf16 MFMA peak)"
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, AMD published peak
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, AMD published peak
 LLC_BYTES = 256 << 20        # MI355X Infinity Cache
 
 
@@ -39,6 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+                    help="decode step (default) or the chunked-prefill step")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (default 2: Llama-3-8B-shaped decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -96,6 +106,116 @@ def cpu_baseline(wl, budget_s):
     }
 
 
+def cpu_baseline_prefill(wl, budget_s):
+    """The oracle's prefill attention, as it stands, one sequence per call
+    (its chunk, context and table) cycling over the workload's sequences
+    until `budget_s` seconds have passed (at least one sequence)."""
+    import resource
+
+    import numpy as np
+
+    from oracle import paged_attention as O
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from plan_oracle import run_oracle
+
+    kp, vp, _, _ = run_oracle(wl, wl.setup + [op for op in wl.step if op[0] != "prefill"])
+    qs = wl.query_start
+    done = flops = 0
+    r0 = resource.getrusage(resource.RUSAGE_SELF)
+    t0 = time.perf_counter()
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        i = done % wl.num_seqs
+        n, L = int(wl.context_lens[i]), int(qs[i + 1] - qs[i])
+        O.prefill_attention(wl.q[qs[i]:qs[i + 1]], kp, vp, wl.tables["final"][i:i + 1],
+                            wl.context_lens[i:i + 1], np.array([0, L], np.int32), wl.scale,
+                            wl.dtype)
+        flops += 4 * (L * (n - L) + L * (L + 1) // 2) * wl.num_q_heads * wl.head_dim
+        done += 1
+    wall = time.perf_counter() - t0
+    r1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    return {
+        "value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": round(cpu / wall, 2),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle prefill, one sequence's chunk per call, {done} "
+                   f"sequences cycling over the {wl.num_seqs} of the same workload: "
+                   f"{wall:.1f} s wall; cores = CPU time / wall time; host affinity "
+                   f"{len(os.sched_getaffinity(0))} cpus"),
+    }
+
+
+def prefill_main(args):
+    import torch
+
+    import workloads as W
+    from workloads.device import DeviceWorkload
+
+    wl = W.make_prefill()
+    dev = DeviceWorkload(wl)
+    dev.run_setup()
+    dev.release_setup_inputs()
+    pool_bytes = 2 * dev.pools[0][0].numel() * dev.pools[0][0].element_size()
+    npools = max(2, min(8, -(-4 * LLC_BYTES // pool_bytes) + 1))
+    dev.add_pool_copies(npools - 1)
+    torch.cuda.synchronize()
+    att_ops = [op for op in dev.step_ops if op[0] == "prefill"]
+    other_ops = [op for op in dev.step_ops if op[0] != "prefill"]
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        pool = k % npools
+        dev._run(other_ops, pool, record_slots=False)
+        if ev is not None:
+            ev[0].record(stream)
+        dev._run(att_ops, pool)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    att_ms = [a.elapsed_time(b) for a, b in events]
+    att_avg = sum(att_ms) / len(att_ms)
+    flops = wl.prefill_flops()
+    achieved = flops / (att_avg * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {
+            "workload": wl.name, "num_seqs": wl.num_seqs,
+            "query_tokens": int(wl.query_start[-1]), "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+            "block_size": wl.block_size, "sum_context_tokens": int(wl.context_lens.sum()),
+            "step_calls": ["pa_write_kv_at", "pa_prefill_attention"],
+            "seed": list(wl.seed), "pool_copies_rotated": npools,
+            "parallelism": "single GPU",
+        },
+        "flops_per_step": flops,
+        "prefill_ms": {"avg": round(att_avg, 5), "min": round(min(att_ms), 5),
+                       "max": round(max(att_ms), 5)},
+        "roofline": {
+            "kernel": "pa_prefill_attention: prefill_flash_kernel (events around the call)",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": flops, "avg_launch_us": round(att_avg * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def measured_traffic(wl):
     """HBM bytes per decode call from the committed counter summary, if it was
     taken on this workload with the decode source as it is now (else None)."""
@@ -151,6 +271,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.workload == "prefill":
+        prefill_main(args)
+        return
     import paged_kv_cache_188_amd as pa
     import workloads as W
     from workloads.device import DeviceWorkload

@@ -92,13 +92,6 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
   return __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)));
 }
 
-// Plain (cached) loads, for data that other waves read again.
-template <bool NT, typename V>
-__device__ __forceinline__ V load_kv(const V* p) {
-  if constexpr (NT) return load_stream(p);
-  else return *p;
-}
-
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
@@ -154,9 +147,8 @@ struct Tile {
 // Load a tile whose 16 tokens lie in one block (BS >= 16): cb is the element
 // offset of the (block, KV head) chunk, o the tile's first token in the
 // block.  If kk >= 0, token kk of the tile is read from the row pair knew /
-// vnew (D elements each) instead of the pools.  NT: non-temporal loads (data
-// read once).
-template <int D, int BS, bool NT = true>
+// vnew (D elements each) instead of the pools.
+template <int D, int BS>
 __device__ __forceinline__ void load_tile(const uint16_t* kpool, const uint16_t* vpool, int64_t cb,
                                           int o, int lane, Tile<D>& b,
                                           const uint16_t* knew = nullptr,
@@ -166,13 +158,13 @@ __device__ __forceinline__ void load_tile(const uint16_t* kpool, const uint16_t*
   const bool k_from_new = col == kk;  // kk = -1: no token is overridden
 #pragma unroll
   for (int s = 0; s < D / 32; ++s)
-    b.k[s] = load_kv<NT>(reinterpret_cast<const uint4*>(
+    b.k[s] = load_stream(reinterpret_cast<const uint4*>(
         k_from_new ? knew + 32 * s + 8 * grp
                    : kpool + cb + ((int64_t)(4 * s + grp) * BS + o + col) * 8));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const bool v_from_new = 4 * grp + j == kk;
-    b.v[j] = load_kv<NT>(reinterpret_cast<const VRowT<D>*>(
+    b.v[j] = load_stream(reinterpret_cast<const VRowT<D>*>(
         v_from_new ? vnew + DV * col : vpool + cb + (int64_t)(o + 4 * grp + j) * D + DV * col));
   }
 }
@@ -182,17 +174,12 @@ __device__ __forceinline__ void load_tile(const uint16_t* kpool, const uint16_t*
 // than kLazyMax, so every weight 2^(x - m_run) stays <= 2^kLazyMax and the
 // common path needs no cross-lane traffic; results are exact either way
 // (partials carry m_run as their reference point).
-//
-// `lim` (per lane, <= valid; default valid) also hides the tile's tokens >=
-// lim from this lane's column: the causal limit of a query token.  Every
-// column must see at least one token of the first tile it attends to.
 template <int D>
 __device__ __forceinline__ void compute_tile(const DecodeParams& p, MfmaState<D>& st,
                                              const bf16x8_t (&qv)[D / 32], Tile<D>& b, int valid,
-                                             int lane, int lim = -1) {
+                                             int lane) {
   constexpr int DV = D / 16;
   const int grp = lane >> 4;
-  if (lim < 0) lim = valid;
   // scores: lane holds head `col`, tokens 4*grp + i of the tile
   f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -202,7 +189,7 @@ __device__ __forceinline__ void compute_tile(const DecodeParams& p, MfmaState<D>
   float x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bool ok = 4 * grp + i < lim;
+    const bool ok = full || (4 * grp + i < valid);
     x[i] = ok ? sc[i] * p.scale_log2 : kNegInf;
   }
   const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -739,107 +726,6 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(co
   }
 }
 
-// ---------------------------------------------------------------------------
-// multi-query (chunked prefill) kernel
-// ---------------------------------------------------------------------------
-
-// One wave per (sequence, KV head, group of tq = 16 / G query tokens).  The
-// 16 matrix-core columns that the decode kernel gives to the G query heads
-// of a KV head are here (query token, head) pairs: column c is token
-// c / G of the group and head c % G.  Query token j of a sequence whose
-// context (chunk included) is n tokens and whose chunk has L tokens sits at
-// position n - L + j and attends to positions 0 .. n - L + j; each column
-// hides the later keys of its tile by its own limit.  Keys are walked from
-// position 0 one 16-token tile at a time, the block ids of 64 blocks at a
-// time fetched one per lane.
-template <int D, int BS>
-__global__ __launch_bounds__(kDecodeWaves * kWave) void prefill_mfma_kernel(
-    const DecodeParams p, const int32_t* __restrict__ query_start, int64_t total_q, int tq,
-    int groups_per_seq) {
-  static_assert(BS >= 16, "tiles lie in one block");
-  const int lane = threadIdx.x % kWave;
-  const int grp = lane >> 4, col = lane & 15;
-  const int64_t item = (int64_t)blockIdx.x * kDecodeWaves + wave_id();
-  const int64_t per_seq = (int64_t)p.num_kv_heads * groups_per_seq;
-  if (item >= (int64_t)p.num_seqs * per_seq) return;
-  const int seq = (int)(item / per_seq);
-  const int kvh = (int)((item % per_seq) / groups_per_seq);
-  const int qg = (int)(item % groups_per_seq);
-  const int q0 = query_start[seq];
-  const int L = query_start[seq + 1] - q0;
-  const int j0 = qg * tq;
-  const int G = p.group;
-  if (q0 < 0 || L < 0 || (int64_t)q0 + L > total_q || j0 >= L) return;
-  const int n = clamp_ctx(p, seq);
-  const int jn = min(tq, L - j0);  // query tokens of this group
-
-  // this lane's column: query token j0 + col / G, head col % G, at position
-  // n - L + j0 + col / G; it sees keys 0 .. position.  A token at a negative
-  // position (a chunk longer than the context) sees none: output zero.
-  const bool col_used = col < jn * G;
-  const int cpos = n - L + j0 + (col_used ? col / G : 0);
-  const bool col_valid = col_used && cpos >= 0;
-  const int cj = j0 + (col_valid ? col / G : 0);
-  const int ch = col_valid ? col % G : 0;
-  bf16x8_t qv[D / 32];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           ((int64_t)(q0 + cj) * p.num_q_heads + (int64_t)kvh * G + ch) * D;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (col_valid) raw = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * grp);
-      qv[s] = as_bf16x8(raw);
-    }
-  }
-  MfmaState<D> st;
-  st.reset();
-  const int last = n - L + j0 + jn - 1;  // the group's last position
-  const int ntiles = last < 0 ? 0 : last / 16 + 1;
-  const uint16_t* kpool = static_cast<const uint16_t*>(p.k_cache);
-  const uint16_t* vpool = static_cast<const uint16_t*>(p.v_cache);
-  const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
-  constexpr int kTilesPerChunk = 64 * BS / 16;  // tiles whose blocks one id per lane covers
-  int ids = 0;
-  for (int t = 0; t < ntiles; ++t) {
-    if (t % kTilesPerChunk == 0) {
-      const int b = (t / kTilesPerChunk) * 64 + lane;
-      int v = 0;
-      if (b * BS <= last) v = bt[b];
-      ids = (v >= 0 && v < p.num_blocks) ? v : 0;  // a bad entry reads block 0
-    }
-    const int phys = __builtin_amdgcn_readlane(ids, ((16 * t) / BS) % 64);
-    Tile<D> b;  // cached loads: the other query groups of the segment read it too
-    load_tile<D, BS, false>(kpool, vpool,
-                            ((int64_t)phys * p.num_kv_heads + kvh) * ((int64_t)BS * D),
-                            (16 * t) % BS, lane, b);
-    const int valid = min(16, n - 16 * t);
-    // unused columns see every token of the tile (zero Q, results dropped)
-    const int lim = col_valid ? max(0, min(valid, cpos + 1 - 16 * t)) : valid;
-    compute_tile<D>(p, st, qv, b, valid, lane, lim);
-  }
-  // normalise and store the columns' rows: out[q0 + token][kvh*G + head][:]
-  constexpr int DV = D / 16;
-  float l_run = st.l_run;
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int c = 4 * grp + r;
-    const float l_c = __shfl(l_run, c);
-    if (c >= jn * G) continue;
-    // l_c >= 1 for a column that sees a key (its largest weight is >= 1)
-    const float inv = n - L + j0 + c / G >= 0 ? 1.0f / l_c : 0.f;
-    float* dst = p.out + ((int64_t)(q0 + j0 + c / G) * p.num_q_heads + (int64_t)kvh * G + c % G) * D +
-                 DV * col;
-#pragma unroll
-    for (int k = 0; k < DV; k += 4)
-      *reinterpret_cast<float4*>(dst + k) = make_float4(st.acc[k][r] * inv, st.acc[k + 1][r] * inv,
-                                                        st.acc[k + 2][r] * inv,
-                                                        st.acc[k + 3][r] * inv);
-  }
-}
-
 template <typename T, int D, int GMAX>
 __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_valu_kernel(const DecodeParams p,
                                                                            int block_size) {
@@ -1155,30 +1041,6 @@ DecodeWorkspace decode_workspace_streamk(int num_seqs, int group, int head_dim) 
   w.acc_off = w.l_off + align256(slots * sizeof(float));
   w.total = w.acc_off + align256(slots * head_dim * sizeof(float));
   return w;
-}
-
-hipError_t launch_prefill(const DecodeParams& p, const int32_t* query_start, int64_t total_q,
-                          int max_query_len, int head_dim, int block_size, hipStream_t stream) {
-  const int tq = p.group >= 16 ? 1 : 16 / p.group;
-  const int groups = (max_query_len + tq - 1) / tq;
-  const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads * groups;
-  if (items == 0) return hipSuccess;
-  const dim3 grid((unsigned)((items + kDecodeWaves - 1) / kDecodeWaves));
-  const dim3 block(kDecodeWaves * kWave);
-#define PA_PREFILL(D_, BS_) \
-  hipLaunchKernelGGL((prefill_mfma_kernel<D_, BS_>), grid, block, 0, stream, p, query_start, \
-                     total_q, tq, groups)
-  if (head_dim == 128) {
-    if (block_size == 16) PA_PREFILL(128, 16);
-    else if (block_size == 32) PA_PREFILL(128, 32);
-    else PA_PREFILL(128, 64);
-  } else {
-    if (block_size == 16) PA_PREFILL(64, 16);
-    else if (block_size == 32) PA_PREFILL(64, 32);
-    else PA_PREFILL(64, 64);
-  }
-#undef PA_PREFILL
-  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, pa_dtype dtype,

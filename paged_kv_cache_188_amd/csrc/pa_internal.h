@@ -94,7 +94,10 @@ DecodePath decode_path(int num_seqs, int block_size, pa_dtype dtype, int partiti
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, pa_dtype dtype,
                          bool vector_only, DecodePath path, hipStream_t stream);
 
-// Multi-query (chunked prefill) attention, bf16, block_size >= 16.
+// Multi-query (chunked prefill) attention, bf16, block_size >= 16: one
+// workgroup per (sequence, KV head, prefill_tokens_per_workgroup(G) chunk
+// tokens).
+int prefill_tokens_per_workgroup(int group);
 hipError_t launch_prefill(const DecodeParams& p, const int32_t* query_start, int64_t total_q,
                           int max_query_len, int head_dim, int block_size, hipStream_t stream);
 

@@ -1,0 +1,428 @@
+// Multi-query (chunked prefill) paged attention for gfx950 (MI355X).
+//
+// What is computed ([bicarait] "Blueprint Arsitektur 3: Chunked Prefill"): a
+// prompt is processed a chunk at a time; chunk token j of a sequence whose
+// context (chunk included) is n tokens and whose chunk has L tokens sits at
+// position n - L + j and attends, with ordinary softmax attention, to the
+// positions 0 .. n - L + j, reached block by block through the sequence's
+// block table exactly as the decode reaches them ([nalar] "Kernel attention
+// harus mengikuti block table").  A token at a negative position (a chunk
+// longer than its context) sees no key; its output is zero.
+//
+// Unlike the decode, this is a dense contraction with reuse: every K/V row of
+// the context is used by every query row of the chunk, so the kernel is
+// built around the matrix cores and keeps K/V tiles in LDS.
+//
+// Work decomposition (a gfx950 design, not on the pages).  A "row" is a
+// (query token, query head) pair; the G = Hq/Hkv heads of a KV head share its
+// K/V, so a workgroup takes the rows of TQ = 128/G consecutive chunk tokens
+// of one (sequence, KV head): 128 rows, token-major (row r = token r / G,
+// head r % G), 32 per wave.  The workgroup walks the keys from position 0 in
+// steps of 32 (two 16-key halves): the 256 threads copy the step's K and V
+// rows from the paged pools into LDS (double-buffered: the next step's loads
+// are in flight while the current one is used), then every wave
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (LDS),
+//                 B = 32 dims x 16 rows (registers, loaded once);
+//                 lane (grp = lane/16, col = lane%16) gets the scores of
+//                 row col for keys 4*grp + i of each 16-key half;
+//   softmax       online, base 2, the scale applied inside the exponent
+//                 (exp2(s*c - m), one fused multiply-add per score), the
+//                 running max moved only when a score passes it by 8 (as in
+//                 the decode); each row hides keys past its own position
+//                 (causal), which only steps on the diagonal need to check;
+//   O += P V      v_mfma_f32_16x16x32_bf16 with A = P (16 rows x 32 keys,
+//                 taken straight from the scores' registers: k index
+//                 8*grp + e is key 4*grp + e of half 0 for e < 4 and of half
+//                 1 for e >= 4) and B = V in the same key order.  P is split
+//                 into hi + lo bf16 parts (hi = upper 16 bits, lo = the
+//                 rounded rest), so the weights keep float32 accuracy;
+//                 bf16 x bf16 products are exact and accumulate in float32.
+//                 Output tile nt: lane holds dims (D/16)*col + nt of rows
+//                 4*grp + r (the decode's dim order).
+// Latency: the block ids of 64 blocks are fetched at once (one per lane),
+// so no K/V load waits for a table lookup; loaded V rows are only inspected
+// (zeroed past the context) when they are stored to LDS a step later; the
+// barrier orders LDS only, so the next step's global loads stay in flight
+// across it.  (Measured on MI355X, the chunked-prefill workload of 16
+// sequences x 512-token chunks: 783 us with one wave per 16 query rows and
+// no K/V sharing, 626 us with this layout.)
+// Workgroups are numbered so that those of one (sequence, KV head) run on
+// one XCD (consecutive workgroup ids are dealt round-robin over the 8 XCDs),
+// sharing that XCD's L2 for the K/V they all read; within a sequence the
+// later query tiles (more keys) start first.
+
+#include <type_traits>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// plain vector types (not the uint4 struct) so that register arrays stay in
+// registers
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kRows = 32 * kWaves;  // rows per workgroup
+constexpr int kStep = 32;           // keys per step
+constexpr float kLazyMax = 8.f;
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kXcds = 8;
+
+// Workgroup barrier that orders LDS only: global loads in flight stay in
+// flight across it (a full __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D>
+using VPiece = typename std::conditional<D == 128, u32x4_t, u32x2_t>::type;  // D/16 bf16
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// hi + lo bf16 split of 8 float32 weights, packed as two A operands
+__device__ __forceinline__ void split_weights(const float (&p)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  uint32_t u[8];
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u[i] = __float_as_uint(p[i]);
+    r[i] = p[i] - __uint_as_float(u[i] & 0xffff0000u);  // exact
+  }
+  u32x4_t h, l;
+  h.x = __builtin_amdgcn_perm(u[1], u[0], 0x07060302u);
+  h.y = __builtin_amdgcn_perm(u[3], u[2], 0x07060302u);
+  h.z = __builtin_amdgcn_perm(u[5], u[4], 0x07060302u);
+  h.w = __builtin_amdgcn_perm(u[7], u[6], 0x07060302u);
+  l.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[0], r[1]}, bf16x2_t));
+  l.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[2], r[3]}, bf16x2_t));
+  l.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[4], r[5]}, bf16x2_t));
+  l.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[6], r[7]}, bf16x2_t));
+  hi = as_bf16x8(h);
+  lo = as_bf16x8(l);
+}
+
+// Global -> register loads of one 16-key half for thread u (0..127) of the
+// half: K chunk c = u + 128 i is granule c / 16 of key c % 16, V chunk c is
+// granule c % (D/8) of key c / (D/8); key0 is the half's first position and
+// phys its physical block.  Every address is inside the pools; V rows past
+// the context are zeroed when stored to LDS (not here: a select on the
+// loaded value would wait for the load).
+template <int D, int BS>
+__device__ __forceinline__ void load_step(const uint16_t* kpool, const uint16_t* vpool, int phys,
+                                          int n, int hkv, int kvh, int key0, int u,
+                                          u32x4_t (&kreg)[D / 64], u32x4_t (&vreg)[D / 64]) {
+  constexpr int GR = D / 8;
+  const int o = key0 % BS;
+  const int64_t cb = ((int64_t)phys * hkv + kvh) * ((int64_t)BS * D);
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const int c = u + 128 * i;
+    kreg[i] = *reinterpret_cast<const u32x4_t*>(kpool + cb +
+                                                ((int64_t)(c >> 4) * BS + o + (c & 15)) * 8);
+    vreg[i] = *reinterpret_cast<const u32x4_t*>(vpool + cb + (int64_t)(o + c / GR) * D +
+                                                (c % GR) * 8);
+  }
+}
+
+// Physical block ids of logical blocks 64*chunk .. 64*chunk + 63, one per
+// lane (entries past the context, or outside the pool, read as block 0).
+template <int BS>
+__device__ __forceinline__ int load_ids(const int32_t* bt, int chunk, int n, int num_blocks,
+                                        int lane) {
+  const int b = chunk * 64 + lane;
+  int v = b * BS < n ? bt[b] : 0;
+  return (v >= 0 && v < num_blocks) ? v : 0;
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
+    const DecodeParams p, const int32_t* __restrict__ query_start, int64_t total_q, int tq,
+    int qtiles, int64_t n_items) {
+  static_assert(BS >= 16 && BS % 16 == 0, "16-key halves lie in one block");
+  constexpr int NS = D / 32;   // 32-dim slices of a row
+  constexpr int DV = D / 16;   // output dims per lane per tile
+  constexpr int GR = D / 8;    // 16-byte granules per row
+  constexpr int HALF = 2 * D;  // 16-byte chunks of K (or V) per 16-key half
+  constexpr int CH = D / 64;   // chunks per thread per half, K and V each
+  // [buffer][K: half, granule, key | V: half, key, granule] in 16-byte units
+  __shared__ u32x4_t smem[2][4 * HALF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, col = lane & 15;
+
+  // workgroup -> (sequence, KV head, query tile)
+  const int64_t per_xcd = (n_items + kXcds - 1) / kXcds;
+  const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= n_items) return;
+  const int64_t per_seq = (int64_t)p.num_kv_heads * qtiles;
+  const int seq = (int)(item / per_seq);
+  const int kvh = (int)((item % per_seq) / qtiles);
+  const int qt = qtiles - 1 - (int)(item % qtiles);
+  const int q0 = query_start[seq];
+  const int L = query_start[seq + 1] - q0;
+  const int j0 = qt * tq;
+  if (q0 < 0 || L < 0 || (int64_t)q0 + L > total_q || j0 >= L) return;  // whole workgroup
+  const int n = min(max(p.context_lens[seq], 0), p.max_tokens);
+  const int G = p.group;
+  const int jn = min(tq, L - j0);  // chunk tokens of this workgroup
+  const int base = n - L + j0;     // position of token j0
+
+  // scores are scaled by c >= 0 inside the exponent (exp2(s*c - m)); a
+  // negative scale is carried by negating Q, which is exact
+  const bool neg = p.scale_log2 < 0.f;
+  const float c = fmaxf(fabsf(p.scale_log2), 1e-30f);
+
+  // this lane's two rows (one per 16-row half of the wave): query, position
+  int pos[2];
+  bool live[2];
+  bf16x8_t qv[2][NS];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = wave * 32 + h * 16 + col;
+    const int tk = rr / G, hd = rr - tk * G;
+    live[h] = rr < jn * G && base + tk >= 0;
+    pos[h] = live[h] ? base + tk : n - 1;  // a dead row sees every key (results dropped)
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                           ((int64_t)(q0 + j0 + (live[h] ? tk : 0)) * p.num_q_heads +
+                            (int64_t)kvh * G + (live[h] ? hd : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4_t raw = u32x4_t{0u, 0u, 0u, 0u};
+      if (live[h]) raw = *reinterpret_cast<const u32x4_t*>(qrow + 32 * s + 8 * grp);
+      if (neg) raw ^= 0x80008000u;
+      qv[h][s] = as_bf16x8(raw);
+    }
+  }
+  // the wave's last live position and its rows' first position (wave-uniform)
+  int wmax = max(live[0] ? pos[0] : -1, live[1] ? pos[1] : -1);
+  int wmin = min(pos[0], pos[1]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    wmax = max(wmax, __shfl_xor(wmax, o));
+    wmin = min(wmin, __shfl_xor(wmin, o));
+  }
+  wmax = __builtin_amdgcn_readfirstlane(wmax);
+  wmin = __builtin_amdgcn_readfirstlane(wmin);
+  const int last = base + jn - 1;  // the workgroup's last position (<= n - 1)
+  const int nsteps = last < 0 ? 0 : last / kStep + 1;
+
+  // global -> register loads of one step: thread (half th, index u)
+  const int th = tid >> 7, u = tid & 127;
+  const uint16_t* kpool = static_cast<const uint16_t*>(p.k_cache);
+  const uint16_t* vpool = static_cast<const uint16_t*>(p.v_cache);
+  const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
+  u32x4_t kreg[CH], vreg[CH];
+  // block ids come 64 at a time, one per lane, and are picked with readlane:
+  // the K/V loads of a step never wait for a table lookup
+  int ids = 0, ids_chunk = -1;
+  auto fetch = [&](int step) {
+    const int key0 = __builtin_amdgcn_readfirstlane(step * kStep + th * 16);
+    const int blk = key0 / BS;
+    if (blk / 64 != ids_chunk) {
+      ids_chunk = blk / 64;
+      ids = load_ids<BS>(bt, ids_chunk, n, p.num_blocks, lane);
+    }
+    load_step<D, BS>(kpool, vpool, __builtin_amdgcn_readlane(ids, blk % 64), n,
+                     p.num_kv_heads, kvh, key0, u, kreg, vreg);
+  };
+  f32x4_t acc[2][DV];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int nt = 0; nt < DV; ++nt) acc[h][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+
+  if (nsteps > 0) fetch(0);
+  for (int step = 0; step < nsteps; ++step) {
+    u32x4_t* buf = smem[step & 1];
+    const int skey0 = step * kStep + th * 16;  // first key of this thread's half
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = u + 128 * i;
+      buf[th * HALF + c] = kreg[i];
+      buf[2 * HALF + th * HALF + c] =
+          skey0 + c / (D / 8) < n ? vreg[i] : u32x4_t{0u, 0u, 0u, 0u};  // keys past the context
+    }
+    lds_barrier();
+    if (step + 1 < nsteps) fetch(step + 1);
+    if (step * kStep > wmax) continue;  // nothing left for this wave's rows
+
+    // S^T = K Q^T: sc[half][row half]; all K operands first, then the four
+    // accumulations interleaved
+    f32x4_t sc[2][2];
+    {
+      bf16x8_t a[2][NS];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) a[kh][s] = as_bf16x8(buf[kh * HALF + (4 * s + grp) * 16 + col]);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sc[kh][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            sc[kh][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kh][s], qv[h][s], sc[kh][h], 0, 0, 0);
+    }
+    // V rows 4*grp + j of each half, dims (D/16)*col .. +D/16-1
+    const VPiece<D>* vb = reinterpret_cast<const VPiece<D>*>(buf + 2 * HALF);
+    VPiece<D> vr[2][4];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vr[kh][j] = vb[(kh * 16 + 4 * grp + j) * 16 + col];
+
+    // softmax: exponent arguments s * c - m (the causal mask only on steps
+    // that reach past some row's position), lazy reference point, P split
+    const bool diag = step * kStep + kStep - 1 > wmin;
+    float x[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[h][4 * kh + i] = sc[kh][h][i];
+    if (diag) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (step * kStep + kh * 16 + 4 * grp + i > pos[h]) x[h][4 * kh + i] = kNegInf;
+    }
+    float lmax[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      lmax[h] = fmaxf(fmaxf(fmaxf(x[h][0], x[h][1]), fmaxf(x[h][2], x[h][3])),
+                      fmaxf(fmaxf(x[h][4], x[h][5]), fmaxf(x[h][6], x[h][7]))) * c;
+    if (__any(lmax[0] > m_run[0] + kLazyMax || lmax[1] > m_run[1] + kLazyMax)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float mt = fmaxf(lmax[h], __shfl_xor(lmax[h], 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run[h], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);  // 0 on the first step
+        l_run[h] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+          for (int nt = 0; nt < DV; ++nt) acc[h][nt][r] *= a;
+        }
+        m_run[h] = m_new;
+      }
+    }
+    bf16x8_t phi[2], plo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float pw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pw[i] = __builtin_amdgcn_exp2f(fmaf(x[h][i], c, -m_run[h]));
+      l_run[h] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+      split_weights(pw, phi[h], plo[h]);
+    }
+    // O += P V: eight independent accumulations between two on the same
+    // accumulator
+#pragma unroll
+    for (int n0 = 0; n0 < DV; n0 += 4) {
+      bf16x8_t bv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int nt = n0 + t;
+        const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+        const int w = nt >> 1;
+        u32x4_t bw;
+        bw.x = __builtin_amdgcn_perm(vr[0][1][w], vr[0][0][w], sel);
+        bw.y = __builtin_amdgcn_perm(vr[0][3][w], vr[0][2][w], sel);
+        bw.z = __builtin_amdgcn_perm(vr[1][1][w], vr[1][0][w], sel);
+        bw.w = __builtin_amdgcn_perm(vr[1][3][w], vr[1][2][w], sel);
+        bv[t] = as_bf16x8(bw);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[h][n0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[h], bv[t], acc[h][n0 + t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[h][n0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[h], bv[t], acc[h][n0 + t], 0, 0, 0);
+    }
+  }
+
+  // normalise and store: acc[h][nt][r] is row wave*32 + 16h + 4*grp + r,
+  // dim (D/16)*col + nt
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float l = l_run[h];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float l_c = __shfl(l, 4 * grp + r);
+      const int rr = wave * 32 + h * 16 + 4 * grp + r;
+      if (rr >= jn * G) continue;
+      const int tk = rr / G, hd = rr - tk * G;
+      // a row that sees a key has l >= 1 (its largest weight is >= 1)
+      const float inv = base + tk >= 0 ? 1.0f / l_c : 0.f;
+      float* dst = p.out + ((int64_t)(q0 + j0 + tk) * p.num_q_heads + (int64_t)kvh * G + hd) * D +
+                   DV * col;
+#pragma unroll
+      for (int k = 0; k < DV; k += 4)
+        *reinterpret_cast<float4*>(dst + k) =
+            make_float4(acc[h][k][r] * inv, acc[h][k + 1][r] * inv, acc[h][k + 2][r] * inv,
+                        acc[h][k + 3][r] * inv);
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, const int32_t* query_start, int64_t total_q, int tq,
+                    int qtiles, int64_t items, int block_size, hipStream_t stream) {
+  // padded to a multiple of the XCD count so that the id mapping is a bijection
+  const int64_t blocks = (items + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (block_size == 16)
+    hipLaunchKernelGGL((prefill_flash_kernel<D, 16>), grid, block, 0, stream, p, query_start,
+                       total_q, tq, qtiles, items);
+  else if (block_size == 32)
+    hipLaunchKernelGGL((prefill_flash_kernel<D, 32>), grid, block, 0, stream, p, query_start,
+                       total_q, tq, qtiles, items);
+  else
+    hipLaunchKernelGGL((prefill_flash_kernel<D, 64>), grid, block, 0, stream, p, query_start,
+                       total_q, tq, qtiles, items);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_tokens_per_workgroup(int group) { return kRows / group; }
+
+hipError_t launch_prefill(const DecodeParams& p, const int32_t* query_start, int64_t total_q,
+                          int max_query_len, int head_dim, int block_size, hipStream_t stream) {
+  const int tq = prefill_tokens_per_workgroup(p.group);
+  const int qtiles = (max_query_len + tq - 1) / tq;
+  const int64_t items = (int64_t)p.num_seqs * p.num_kv_heads * qtiles;
+  if (items == 0) return hipSuccess;
+  return head_dim == 128
+             ? launch_d<128>(p, query_start, total_q, tq, qtiles, items, block_size, stream)
+             : launch_d<64>(p, query_start, total_q, tq, qtiles, items, block_size, stream);
+}
+
+}  // namespace pa
