@@ -352,3 +352,32 @@ def prefill_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                 den = np.where(seen, w.sum(axis=1), 1.0)
                 out[qs[i]:qs[i + 1], h] = (w @ v_t) / den[:, None]
     return out
+
+
+# ---------------------------------------------------------------------------
+# block swap between two pools (eviction to host memory and return)
+# ---------------------------------------------------------------------------
+
+def swap_blocks(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray, src_v: np.ndarray,
+                pairs: np.ndarray):
+    """Return copies of the destination pools where block ``dst`` holds block
+    ``src`` of the source pools, for each (src, dst) pair.
+
+    [gyaansetu] "How PagedAttention fixes this" (fine-grained eviction):
+    fixed-size pages, not whole sequences, move between GPU and CPU memory.
+    Moving a page changes where its bytes live, never the bytes.  Both pool
+    pairs have the same block shape; a pair naming a block outside its pool is
+    a contract error here (the GPU skips it).
+    """
+    if src_k.shape[1:] != dst_k.shape[1:] or src_v.shape[1:] != dst_v.shape[1:]:
+        raise ContractError("the pools disagree in block shape")
+    k_out, v_out = dst_k.copy(), dst_v.copy()
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if len(set(pairs[:, 1].tolist())) != len(pairs):
+        raise ContractError("destinations must be distinct")
+    for s, d in pairs:
+        if not (0 <= s < src_k.shape[0]) or not (0 <= d < dst_k.shape[0]):
+            raise ContractError("pair outside a pool")
+        k_out[d] = src_k[s]
+        v_out[d] = src_v[s]
+    return k_out, v_out

@@ -531,7 +531,38 @@ def pin_prefill_chunks_compose(O):
         assert np.max(np.abs(dec[0] - whole[pos])) <= 1e-13
 
 
+def pin_swap(O):
+    """[gyaansetu] "How PagedAttention fixes this" (fine-grained eviction):
+    a page moved to host memory and back holds the same bytes; nothing else
+    moves; attention through the new placement is unchanged, bit for bit."""
+    rng = np.random.default_rng(61)
+    c = random_case(rng, num_seqs=2, hq=4, hkv=2, d=4, bs=4, ctx_max=0, dtype="bf16",
+                    ctx=[9, 6], x=2, slack=4)
+    kp, vp, t = c["kp"], c["vp"], c["tables"]
+    hk = nan_like_pool((6,) + kp.shape[1:], "bf16")
+    hv = nan_like_pool((6,) + vp.shape[1:], "bf16")
+    out_pairs = np.array([[t[0, 0], 4], [t[0, 1], 0], [t[0, 2], 5]], np.int32)
+    hk2, hv2 = O.swap_blocks(hk, hv, kp, vp, out_pairs)
+    for s_, d_ in out_pairs:
+        assert hk2[d_].tobytes() == kp[s_].tobytes() and hv2[d_].tobytes() == vp[s_].tobytes()
+    for b in (1, 2, 3):                                    # untouched host blocks
+        assert hk2[b].tobytes() == hk[b].tobytes() and hv2[b].tobytes() == hv[b].tobytes()
+    # back into free device blocks (the ones past the two tables' blocks)
+    used = set(t[t >= 0].tolist())
+    free = [b for b in range(kp.shape[0]) if b not in used][:3]
+    in_pairs = np.array([[4, free[0]], [0, free[1]], [5, free[2]]], np.int32)
+    kp2, vp2 = O.swap_blocks(kp, vp, hk2, hv2, in_pairs)
+    t2 = t.copy()
+    t2[0, :3] = free
+    a = O.decode_attention(c["q"], kp, vp, t, c["ctx"], 0.5, "bf16")
+    b = O.decode_attention(c["q"], kp2, vp2, t2, c["ctx"], 0.5, "bf16")
+    assert a.tobytes() == b.tobytes()
+    for blk in range(kp.shape[0]):                         # only the targets changed
+        if blk not in free:
+            assert kp2[blk].tobytes() == kp[blk].tobytes()
+
+
 ALL_PINS = [pin_value_decoding, pin_worked_tables, pin_slot_bijection, pin_write_bruteforce,
             pin_write_roundtrip, pin_copy, pin_attention_dense, pin_attention_sdpa,
             pin_closed_forms, pin_shared_vs_private, pin_cow_isolation, pin_prefill_bruteforce,
-            pin_prefill_sdpa, pin_prefill_chunks_compose]
+            pin_prefill_sdpa, pin_prefill_chunks_compose, pin_swap]

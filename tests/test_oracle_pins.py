@@ -123,6 +123,7 @@ MUTATIONS = {
         "k_new[j].reshape(num_kv_heads, x, head_dim // x).transpose(0, 2, 1)"),
     "copy-reversed": ("k_out[d] = k_pool[s]", "k_out[s] = k_pool[d]"),
     "scale-not-float32": ("np.float64(np.float32(scale))", "np.float64(scale) * 1.001"),
+    "swap-reversed": ("k_out[d] = src_k[s]", "k_out[d] = src_k[d]"),
     "prefill-causal-off-by-one": ("t[None, :] <= pos[:, None]", "t[None, :] < pos[:, None]"),
     "prefill-chunk-at-start": ("pos = n - L + np.arange(L)", "pos = np.arange(L)"),
     "prefill-heads-interleaved": ("range(g * group, (g + 1) * group)",
