@@ -22,6 +22,12 @@ launch on the stream it runs on) and the CPU oracle's rate on a bounded sample.
 measures the chunked-prefill step instead (the chunk's K/V stored with
 pa_write_kv_at, then pa_prefill_attention): useful TFLOP/s of the causal
 attention against the bf16 matrix-core peak.
+
+    python bench.py --workload swap
+
+measures pa_swap_blocks: 8192 blocks (512 MiB of K and V) out to pinned
+host memory and back, against the PCIe 5.0 x16 peak and a contiguous
+torch copy of the same bytes (the DMA engines' rate on this machine).
 """
 
 from __future__ import annotations
@@ -37,7 +43,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seq-steps/sec"
 PREFILL_METRIC = "chunked-prefill paged attention: useful TFLOP/s (causal, % of bf16 MFMA peak)"
+SWAP_METRIC = "block swap HBM <-> pinned host memory: GB/s per direction"
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, AMD published peak
+HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, AMD published peak
 LLC_BYTES = 256 << 20        # MI355X Infinity Cache
 
@@ -47,8 +55,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
-                    help="decode step (default) or the chunked-prefill step")
+    ap.add_argument("--workload", choices=["decode", "prefill", "swap"], default="decode",
+                    help="decode step (default), the chunked-prefill step, or block swap")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (default 2: Llama-3-8B-shaped decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -216,6 +224,71 @@ def prefill_main(args):
     print(json.dumps(res), flush=True)
 
 
+def swap_main(args):
+    """Swap-out of every block of a 512 MiB pool pair to pinned host pools,
+    then swap-in to a permuted placement; per-direction GB/s from HIP events
+    on the stream, next to a contiguous torch copy of the same size."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_188_amd as pa
+    nb, hkv, bs, d = 8192, 8, 16, 128
+    kd = torch.randn((nb, hkv, d // 8, bs, 8), device="cuda").to(torch.bfloat16)
+    vd = torch.randn((nb, hkv, bs, d), device="cuda").to(torch.bfloat16)
+    hk = torch.empty(kd.shape, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(vd.shape, dtype=torch.bfloat16, pin_memory=True)
+    rng = np.random.default_rng(188)
+    out_pairs = torch.from_numpy(np.stack([np.arange(nb), rng.permutation(nb)], 1)
+                                 .astype(np.int32)).cuda()
+    in_pairs = torch.from_numpy(np.stack([rng.permutation(nb), np.arange(nb)], 1)
+                                .astype(np.int32)).cuda()
+    nbytes = 2 * kd.numel() * kd.element_size()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+    reps = max(1, min(args.steps, 10))
+    t_out = timed(lambda: pa.swap_blocks(hk, hv, kd, vd, out_pairs), reps)
+    t_in = timed(lambda: pa.swap_blocks(kd, vd, hk, hv, in_pairs), reps)
+    flat_d = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    flat_h = torch.empty(nbytes // 2, dtype=torch.bfloat16, pin_memory=True)
+    t_d2h = timed(lambda: flat_h.copy_(flat_d, non_blocking=True), reps)
+    t_h2d = timed(lambda: flat_d.copy_(flat_h, non_blocking=True), reps)
+    gbs = lambda ms: nbytes / (ms * 1e-3) / 1e9
+    out_rate, in_rate = gbs(t_out), gbs(t_in)
+    res = {
+        "metric": SWAP_METRIC, "value": round(min(out_rate, in_rate), 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": reps, "warmup": 2, "ms_per_step": round(t_out + t_in, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"swap {nb} blocks (Hkv={hkv} bs={bs} D={d} bf16, K and V: "
+                               f"{nbytes >> 20} MiB) out to pinned host memory and back",
+                   "parallelism": "single GPU"},
+        "swap_out_gbs": round(out_rate, 2), "swap_in_gbs": round(in_rate, 2),
+        "torch_copy_d2h_gbs": round(gbs(t_d2h), 2), "torch_copy_h2d_gbs": round(gbs(t_h2d), 2),
+        "roofline": {
+            "kernel": "pa_swap_blocks: copy_blocks_kernel over the host link (events per call)",
+            "bound": "host link", "achieved": round(min(out_rate, in_rate), 2),
+            "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(min(out_rate, in_rate) / HOST_LINK_PEAK_GBPS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": nbytes,
+            "avg_launch_us": {"out": round(t_out * 1e3, 1), "in": round(t_in * 1e3, 1)},
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
 def measured_traffic(wl):
     """HBM bytes per decode call from the committed counter summary, if it was
     taken on this workload with the decode source as it is now (else None)."""
@@ -273,6 +346,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "prefill":
         prefill_main(args)
+        return
+    if args.workload == "swap":
+        swap_main(args)
         return
     import paged_kv_cache_188_amd as pa
     import workloads as W

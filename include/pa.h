@@ -8,6 +8,8 @@
  *   pa_write_kv          store new tokens' K/V in their slots
  *   pa_write_kv_at       the two above in one launch
  *   pa_copy_blocks       copy whole KV blocks (copy-on-write of shared blocks)
+ *   pa_swap_blocks       move whole KV blocks between two pools, e.g. HBM and
+ *                        pinned host memory (fine-grained eviction)
  *   pa_decode_attention  one query token per sequence attends to its history,
  *                        reached block by block through its block table
  *   pa_decode_attention_append  the new tokens stored and attended in one call
@@ -179,6 +181,35 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache,
                          int32_t num_blocks, int32_t block_size,
                          int32_t num_kv_heads, int32_t head_dim,
                          pa_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_swap_blocks  (block-granular eviction to, and return from, host memory)
+ *
+ * [gyaansetu] "The memory problem" and "How PagedAttention fixes this": when
+ * HBM runs out, whole sequences need not leave the GPU; small fixed-size
+ * pages are moved to CPU memory and brought back.  For each pair n: block
+ * dst = block_mapping[n][1] of the destination pools (dst_k, dst_v) receives
+ * every KV head of block src = block_mapping[n][0] of the source pools
+ * (src_k, src_v); bit copy, one layer per call.  Both pool pairs have the
+ * layout of pa.h with the same block_size, num_kv_heads, head_dim and
+ * element type; they may have different block counts.  Each of the four pool
+ * pointers may be device memory of the current device or pinned host memory
+ * (hipHostMalloc; the kernel reads and writes it directly over the host
+ * link); block_mapping is int32 [num_pairs][2] in either.  Any other pointer
+ * (pageable host memory, another device's memory) gives PA_ERR_UNSUPPORTED
+ * before anything is launched.  Swap-out: src = the device pools,
+ * dst = the host pools; swap-in: the reverse.  Pairs naming a block outside
+ * its pool are skipped.  Destinations must be distinct.  The source and
+ * destination pools must be different allocations (PA_ERR_SHAPE when a
+ * source and destination pointer are equal; use pa_copy_blocks within a
+ * pool).  Results are visible to the host after the stream synchronises.
+ * ------------------------------------------------------------------------- */
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k,
+                         const void* src_v, const int32_t* block_mapping,
+                         int32_t num_pairs, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                         void* stream);
 
 /* ---------------------------------------------------------------------------
  * pa_decode_attention

@@ -39,13 +39,18 @@ class BMStats(ctypes.Structure):
                 ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
                 ("live_sequences", ctypes.c_int32), ("logical_blocks", ctypes.c_int64),
                 ("logical_tokens", ctypes.c_int64), ("stored_tokens", ctypes.c_int64),
-                ("physical_slots", ctypes.c_int64)]
+                ("physical_slots", ctypes.c_int64), ("swapped_sequences", ctypes.c_int32),
+                ("num_host_blocks", ctypes.c_int32), ("free_host_blocks", ctypes.c_int32)]
 
 
 SIGNATURES = {
     "pa_abi_version": (_I32, []),
     "pa_bm_create": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_void_p)]),
+    "pa_bm_create_with_host": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32,
+                                              ctypes.POINTER(ctypes.c_void_p)]),
     "pa_bm_destroy": (None, [_P]),
+    "pa_bm_swap_out": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
+    "pa_bm_swap_in": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
     "pa_bm_add_sequence": (ctypes.c_int, [_P, _P]),
     "pa_bm_fork": (ctypes.c_int, [_P, _I32, _P]),
     "pa_bm_free_sequence": (ctypes.c_int, [_P, _I32]),
@@ -59,6 +64,8 @@ SIGNATURES = {
     "pa_write_kv_at": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _I64, _I32,
                                       _I32, _I32, _I32, ctypes.c_int, _P, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _P]),
+    "pa_swap_blocks": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                      ctypes.c_int, _P]),
     "pa_decode_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "pa_decode_streamk_workers": (_I32, [_I32, _I32, _I32, _I32, ctypes.c_int, ctypes.c_uint32]),
     "pa_decode_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -232,6 +239,38 @@ def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
         _dtype_code(k_cache), _stream(stream)))
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None):
+    """For each (src, dst) row of block_mapping [n][2] (a device int32
+    tensor): block dst of (dst_k, dst_v) := block src of (src_k, src_v).
+    Either pool pair may be pinned host tensors (pin_memory=True)."""
+    import torch
+    dnb, hkv, bs, d = _host_or_device_pools(dst_k, dst_v)
+    snb, hkv2, bs2, d2 = _host_or_device_pools(src_k, src_v)
+    if (hkv, bs, d) != (hkv2, bs2, d2) or dst_k.dtype != src_k.dtype:
+        raise ValueError("the two pool pairs disagree in block shape or element type")
+    _need(block_mapping, torch.int32, "block_mapping")
+    n = block_mapping.numel() // 2
+    _check("pa_swap_blocks", lib().pa_swap_blocks(
+        _ptr(dst_k), _ptr(dst_v), _ptr(src_k), _ptr(src_v), _ptr(block_mapping), n, snb, dnb,
+        bs, hkv, d, _dtype_code(src_k), _stream(stream)))
+
+
+def _host_or_device_pools(k_cache, v_cache):
+    """_pools for a pool pair in device memory or in pinned host memory."""
+    if not (k_cache.is_cuda and v_cache.is_cuda):
+        if not (k_cache.is_pinned() and v_cache.is_pinned()):
+            raise TypeError("host pools must be pinned (pin_memory=True)")
+        if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+            raise TypeError("pools must be contiguous")
+        if k_cache.dim() != 5 or v_cache.dim() != 4:
+            raise ValueError("K pool must be [NB][Hkv][D/x][bs][x] and V pool [NB][Hkv][bs][D]")
+        nb, hkv, dx, bs, x = k_cache.shape
+        if x * k_cache.element_size() != 16 or tuple(v_cache.shape) != (nb, hkv, bs, dx * x):
+            raise ValueError("K and V pools disagree")
+        return nb, hkv, bs, dx * x
+    return _pools(k_cache, v_cache)
+
+
 def decode_partition_size(num_seqs, num_kv_heads, block_size, max_context_len, partition_size=0):
     return int(lib().pa_decode_partition_size(num_seqs, num_kv_heads, block_size,
                                               max_context_len, partition_size))
@@ -340,12 +379,13 @@ class BlockManager:
     block tables, reference counts and copy-on-write; its slots, copy pairs
     and tables feed write_kv, copy_blocks and decode_attention."""
 
-    def __init__(self, num_blocks, block_size, max_seqs, max_blocks_per_seq):
+    def __init__(self, num_blocks, block_size, max_seqs, max_blocks_per_seq, num_host_blocks=0):
         self.block_size = block_size
         self.max_blocks_per_seq = max_blocks_per_seq
         h = ctypes.c_void_p()
-        _check("pa_bm_create", lib().pa_bm_create(num_blocks, block_size, max_seqs,
-                                                  max_blocks_per_seq, ctypes.byref(h)))
+        _check("pa_bm_create_with_host", lib().pa_bm_create_with_host(
+            num_blocks, num_host_blocks, block_size, max_seqs, max_blocks_per_seq,
+            ctypes.byref(h)))
         self._h = h
 
     def close(self):
@@ -387,6 +427,23 @@ class BlockManager:
             self._h, ids.ctypes.data, cnt.ctypes.data, ids.size, slots.ctypes.data,
             pairs.ctypes.data, ctypes.byref(ncopy)))
         return slots, pairs[:ncopy.value].copy()
+
+    def _move(self, fn, seq_ids):
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        pairs = np.empty((max(1, ids.size * self.max_blocks_per_seq), 2), dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(fn, getattr(lib(), fn)(self._h, ids.ctypes.data, ids.size, pairs.ctypes.data,
+                                      ctypes.byref(n)))
+        return pairs[:n.value].copy()
+
+    def swap_out(self, seq_ids):
+        """Swap the sequences out; (GPU block, host block) pairs int32 [k][2]."""
+        return self._move("pa_bm_swap_out", seq_ids)
+
+    def swap_in(self, seq_ids):
+        """Swap the sequences back in; (host block, GPU block) pairs."""
+        return self._move("pa_bm_swap_in", seq_ids)
 
     def tables(self, seq_ids):
         """(tables int32 [n][max_blocks_per_seq] padded with -1, lengths int32 [n])."""

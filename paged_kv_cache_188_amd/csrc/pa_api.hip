@@ -166,8 +166,67 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapp
   if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
   const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
-  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_blocks,
-                                         block_bytes, static_cast<hipStream_t>(stream)));
+  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, block_mapping,
+                                         num_pairs, num_blocks, num_blocks, block_bytes,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// The address the current device uses for p: p itself for its own device
+// memory, the mapped address for pinned host memory.  False for pageable
+// host memory, another device's memory, or an unknown pointer (the kernel
+// must never touch an address it cannot reach).
+bool device_address(const void* p, const void** out) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the query's error for the launch check
+    return false;
+  }
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return false;
+  if (a.isManaged) {
+    *out = p;
+    return true;
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    if (a.device != cur) return false;
+    *out = p;
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer) {
+    const char* host = static_cast<const char*>(a.hostPointer ? a.hostPointer : p);
+    *out = static_cast<const char*>(a.devicePointer) + (static_cast<const char*>(p) - host);
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                         const int32_t* block_mapping, int32_t num_pairs, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_pairs < 0 || src_num_blocks < 1 || dst_num_blocks < 1 || num_kv_heads < 1)
+    return PA_ERR_SHAPE;
+  if (!supported_block_size(block_size) || !supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !block_mapping) return PA_ERR_NULL;
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v))
+    return PA_ERR_UNSUPPORTED;
+  if (dst_k == src_k || dst_v == src_v) return PA_ERR_SHAPE;  // within one pool: pa_copy_blocks
+  const void *dk, *dv, *sk, *sv, *map;
+  if (!device_address(dst_k, &dk) || !device_address(dst_v, &dv) ||
+      !device_address(src_k, &sk) || !device_address(src_v, &sv) ||
+      !device_address(block_mapping, &map))
+    return PA_ERR_UNSUPPORTED;  // not reachable from this device
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  return from_hip(pa::launch_copy_blocks(const_cast<void*>(dk), const_cast<void*>(dv), sk, sv,
+                                         static_cast<const int32_t*>(map), num_pairs,
+                                         src_num_blocks, dst_num_blocks, block_bytes,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,

@@ -120,16 +120,20 @@ constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 constexpr int64_t kCopyPieceBytes = (int64_t)kCopyThreads * kCopyUnroll * 16;
 
+// Block src of the source pools -> block dst of the destination pools (the
+// same pools for a copy-on-write copy; a device pool and a pinned host pool
+// for a swap, which the kernel reaches directly over the host link).
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
-    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-    const int32_t* __restrict__ block_mapping, int num_blocks, int64_t block_bytes) {
+    uint8_t* dst_k, uint8_t* dst_v, const uint8_t* src_k, const uint8_t* src_v,
+    const int32_t* __restrict__ block_mapping, int src_blocks, int dst_blocks,
+    int64_t block_bytes) {
   const int pair = blockIdx.x;
   const int src = block_mapping[2 * pair];
   const int dst = block_mapping[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  uint8_t* base = blockIdx.y ? v_cache : k_cache;
-  const uint4* s = reinterpret_cast<const uint4*>(base + (int64_t)src * block_bytes);
-  uint4* d = reinterpret_cast<uint4*>(base + (int64_t)dst * block_bytes);
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4* s = reinterpret_cast<const uint4*>((blockIdx.y ? src_v : src_k) +
+                                                  (int64_t)src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>((blockIdx.y ? dst_v : dst_k) + (int64_t)dst * block_bytes);
   const int64_t n = block_bytes / 16;
   const int64_t first = (int64_t)blockIdx.z * (kCopyPieceBytes / 16) + threadIdx.x;
   uint4 r[kCopyUnroll];
@@ -228,14 +232,15 @@ hipError_t launch_write_kv_at(void* k_cache, void* v_cache, const void* k_new, c
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
-                              int num_pairs, int num_blocks, int64_t block_bytes,
-                              hipStream_t stream) {
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* block_mapping, int num_pairs, int src_blocks,
+                              int dst_blocks, int64_t block_bytes, hipStream_t stream) {
   if (num_pairs == 0) return hipSuccess;
   const int pieces = (int)((block_bytes + kCopyPieceBytes - 1) / kCopyPieceBytes);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2, pieces), dim3(kCopyThreads), 0,
-                     stream, static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
-                     block_mapping, num_blocks, block_bytes);
+                     stream, static_cast<uint8_t*>(dst_k), static_cast<uint8_t*>(dst_v),
+                     static_cast<const uint8_t*>(src_k), static_cast<const uint8_t*>(src_v),
+                     block_mapping, src_blocks, dst_blocks, block_bytes);
   return hipGetLastError();
 }
 

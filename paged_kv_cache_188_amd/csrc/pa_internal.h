@@ -38,9 +38,11 @@ hipError_t launch_append_kv(void* k_cache, void* v_cache, const void* k_new, con
                             int num_blocks, int block_size, int num_kv_heads, int head_bytes,
                             hipStream_t stream);
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
-                              int num_pairs, int num_blocks, int64_t block_bytes,
-                              hipStream_t stream);
+// Block block_mapping[n][0] of the source pools -> block block_mapping[n][1]
+// of the destination pools (pairs outside either pool are skipped).
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* block_mapping, int num_pairs, int src_blocks,
+                              int dst_blocks, int64_t block_bytes, hipStream_t stream);
 
 struct DecodeParams {
   float* out;

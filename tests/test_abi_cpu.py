@@ -144,6 +144,25 @@ def test_prefill_validation(lib):
     assert _prefill(lib, max_q=0, out=NULL) == OK
 
 
+def test_swap_validation(lib):
+    sw = lambda **k: lib.pa_swap_blocks(
+        k.get("dk", FAKE), k.get("dv", FAKE), k.get("sk", ctypes.c_void_p(0x20000)),
+        k.get("sv", ctypes.c_void_p(0x30000)), k.get("map", FAKE), k.get("n", 3),
+        k.get("snb", 10), k.get("dnb", 10), k.get("bs", 16), k.get("hkv", 2), k.get("d", 128),
+        k.get("dtype", 1), NULL)
+    assert sw(dtype=5) == DTYPE
+    assert sw(n=-1) == SHAPE
+    assert sw(snb=0) == SHAPE
+    assert sw(hkv=0) == SHAPE
+    assert sw(bs=12) == UNSUP
+    assert sw(d=96) == UNSUP
+    assert sw(n=0, dk=NULL) == OK                 # nothing to do
+    assert sw(map=NULL) == NUL
+    assert sw(sv=NULL) == NUL
+    assert sw(dk=MISALIGNED) == UNSUP
+    assert sw(sk=FAKE) == SHAPE                   # source and destination the same pool
+
+
 def test_workspace_and_partition_rules(lib):
     # the library's partition choice (see pa_api.hip): 8B-shaped decode -> 512
     assert pa.decode_partition_size(64, 8, 16, 4096) == 512
