@@ -232,8 +232,8 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k,
  * sizes the fixed-partition grid and workspace (a larger bound is correct,
  * just slower).
  *
- * Work decomposition.  With partition_size == 0, bf16 K/V, flags == 0,
- * block_size >= 16 and num_seqs <= 8192 the library splits the (sequence, KV head, 16-token tile)
+ * Work decomposition.  With partition_size == 0, bf16 K/V, flags == 0 and
+ * num_seqs <= 8192 the library splits the (sequence, KV head, 16-token tile)
  * work evenly over one wave per resident wave slot of the device
  * ("stream-K"); a context shared by two waves is merged from float32
  * partials with an exact log-sum-exp rescale.  Otherwise each context is cut

@@ -23,6 +23,8 @@
 //   * fixed-partition path (float32 K/V, an explicit partition size, or very
 //     large batches): one wave per (segment, partition) work item, partials
 //     merged by decode_reduce_kernel.
+//   With 8-token blocks a 16-token tile covers two blocks; both ids travel in
+//   the tile descriptor.
 //
 // Matrix-core tile loop (bf16 K/V):
 //   a tile is 16 consecutive logical tokens.  Loads are laid out so that
@@ -166,6 +168,34 @@ __device__ __forceinline__ void load_tile(const uint16_t* kpool, const uint16_t*
     const bool v_from_new = 4 * grp + j == kk;
     b.v[j] = load_stream(reinterpret_cast<const VRowT<D>*>(
         v_from_new ? vnew + DV * col : vpool + cb + (int64_t)(o + 4 * grp + j) * D + DV * col));
+  }
+}
+
+// Load a tile that spans two blocks (BS < 16, so BS = 8 and the tile starts
+// a block): tokens 0 .. BS-1 from the chunk at cb0, the rest from cb1.  The
+// new-row override is as in load_tile.
+template <int D, int BS>
+__device__ __forceinline__ void load_tile2(const uint16_t* kpool, const uint16_t* vpool,
+                                           int64_t cb0, int64_t cb1, int lane, Tile<D>& b,
+                                           const uint16_t* knew = nullptr,
+                                           const uint16_t* vnew = nullptr, int kk = -1) {
+  static_assert(16 % BS == 0 && BS < 16, "a tile covers whole blocks");
+  constexpr int DV = D / 16;
+  const int grp = lane >> 4, col = lane & 15;
+  const bool k_from_new = col == kk;
+  const int64_t kb = col < BS ? cb0 : cb1;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+    b.k[s] = load_stream(reinterpret_cast<const uint4*>(
+        k_from_new ? knew + 32 * s + 8 * grp
+                   : kpool + kb + ((int64_t)(4 * s + grp) * BS + col % BS) * 8));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * grp + j;
+    const bool v_from_new = r == kk;
+    b.v[j] = load_stream(reinterpret_cast<const VRowT<D>*>(
+        v_from_new ? vnew + DV * col
+                   : vpool + (r < BS ? cb0 : cb1) + (int64_t)(r % BS) * D + DV * col));
   }
 }
 
@@ -432,10 +462,12 @@ __device__ __forceinline__ Pos advance(Pos q, int k, const int* s_prefix, int S,
 // tile's loads are issued, so building a chunk never waits for memory.
 struct TileDescs {
   int seq, kvh, t, phys_raw, n_raw;
+  int phys_raw2;  // block size 8: the block of the tile's second half
   // Make the values register-resident at this point of the program, so the
   // per-tile reads of a chunk never wait for memory where control flow joins.
   __device__ __forceinline__ void settle() {
-    asm volatile("" : "+v"(seq), "+v"(kvh), "+v"(t), "+v"(phys_raw), "+v"(n_raw));
+    asm volatile("" : "+v"(seq), "+v"(kvh), "+v"(t), "+v"(phys_raw), "+v"(n_raw),
+                 "+v"(phys_raw2));
   }
 };
 
@@ -449,14 +481,17 @@ __device__ __forceinline__ bool n_raw_ok(const TileDescs& d, int l, const Decode
 template <int BS>
 __device__ __forceinline__ TileDescs describe_tiles(const DecodeParams& p, const int* s_prefix,
                                                     Pos start, int count, int lane) {
-  TileDescs d{0, 0, 0, 0, 0};
+  TileDescs d{0, 0, 0, 0, 0, 0};
   if (lane < count) {
     const Pos q = advance(start, lane, s_prefix, p.num_seqs, p.num_kv_heads);
     d.seq = q.seq;
     d.kvh = q.kvh;
     d.t = q.t;
     d.n_raw = p.context_lens[q.seq];
-    d.phys_raw = p.block_tables[(int64_t)q.seq * p.max_blocks_per_seq + (16 * q.t) / BS];
+    const int32_t* row = p.block_tables + (int64_t)q.seq * p.max_blocks_per_seq;
+    d.phys_raw = row[(16 * q.t) / BS];
+    if constexpr (BS < 16)  // the second block, when the table has one
+      d.phys_raw2 = (16 * q.t) / BS + 1 < p.max_blocks_per_seq ? row[(16 * q.t) / BS + 1] : -1;
   }
   return d;
 }
@@ -464,7 +499,7 @@ __device__ __forceinline__ TileDescs describe_tiles(const DecodeParams& p, const
 template <int D, int BS>
 __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_kernel(
     const DecodeParams p) {
-  static_assert(BS >= 16, "stream-K tiles lie in one block");
+  static_assert(BS >= 16 || BS == 8, "a tile lies in one block, or covers two of 8");
   extern __shared__ int s_prefix[];  // [S+1]
   tile_prefix(p, s_prefix);
   const int S = p.num_seqs;
@@ -510,7 +545,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
   TileDescs dc = describe_tiles<BS>(p, s_prefix, pos0, chunk_count(0), lane);
   dc.settle();
   Pos next_pos = advance(pos0, kWave, s_prefix, S, Hkv);
-  TileDescs dn = {0, 0, 0, 0, 0};
+  TileDescs dn = {0, 0, 0, 0, 0, 0};
   if (ntiles > kWave) {
     dn = describe_tiles<BS>(p, s_prefix, next_pos, chunk_count(1), lane);
     next_pos = advance(next_pos, kWave, s_prefix, S, Hkv);
@@ -588,9 +623,19 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
     const bool append = p.k_new != nullptr && valid == n - 16 * t && n_raw_ok(dc, l, p);
     const int64_t row = (int64_t)seq * p.new_stride + (int64_t)kvh * D;
     Tile<D> b;
-    load_tile<D, BS>(kpool, vpool, cb, (16 * t) % BS, lane, b,
-                     static_cast<const uint16_t*>(p.k_new) + row,
-                     static_cast<const uint16_t*>(p.v_new) + row, append ? valid - 1 : -1);
+    if constexpr (BS >= 16) {
+      load_tile<D, BS>(kpool, vpool, cb, (16 * t) % BS, lane, b,
+                       static_cast<const uint16_t*>(p.k_new) + row,
+                       static_cast<const uint16_t*>(p.v_new) + row, append ? valid - 1 : -1);
+    } else {
+      // a short tile's second block may be absent from the table: its rows
+      // are masked, so block 0 stands in
+      int phys2 = __builtin_amdgcn_readlane(dc.phys_raw2, l);
+      phys2 = (phys2 >= 0 && phys2 < p.num_blocks) ? phys2 : 0;
+      load_tile2<D, BS>(kpool, vpool, cb, ((int64_t)phys2 * Hkv + kvh) * ((int64_t)BS * D), lane,
+                        b, static_cast<const uint16_t*>(p.k_new) + row,
+                        static_cast<const uint16_t*>(p.v_new) + row, append ? valid - 1 : -1);
+    }
     compute_tile<D>(p, st, qv, b, valid, lane);
     cur_tlast = t;
   }
@@ -957,6 +1002,7 @@ hipError_t launch_streamk(const DecodeParams& p, hipStream_t stream) {
 template <int D>
 hipError_t launch_streamk_bs(const DecodeParams& p, int block_size, hipStream_t stream) {
   switch (block_size) {
+    case 8: return launch_streamk<D, 8>(p, stream);
     case 16: return launch_streamk<D, 16>(p, stream);
     case 32: return launch_streamk<D, 32>(p, stream);
     default: return launch_streamk<D, 64>(p, stream);
@@ -1014,7 +1060,7 @@ int streamk_workers_per_cu(int head_dim) {
 DecodePath decode_path(int num_seqs, int block_size, pa_dtype dtype, int partition_size,
                        bool vector_only) {
   if (dtype == PA_BF16 && !vector_only && partition_size == 0 && num_seqs <= kStreamKMaxSeqs &&
-      block_size >= 16)
+      block_size >= 8)
     return DecodePath::kStreamK;
   return DecodePath::kPartition;
 }

@@ -190,11 +190,12 @@ def test_workspace_and_partition_rules(lib):
     assert pa.decode_workspace_size(s, hq, 8, d, 32, 131072, vector_only=True) == \
         pa.decode_workspace_size(s, hq, 8, d, 32, 131072, dtype=f32)
     assert _decode(lib, ws=FAKE, ws_bytes=0) == WS        # stream-K always needs its workspace
-    # which path: float32, an explicit partition, block size 8 and the vector
-    # kernel take fixed partitions (answered without a GPU)
+    # which path: float32, an explicit partition, the vector kernel and very
+    # large batches take fixed partitions (answered without a GPU)
     assert lib.pa_decode_streamk_workers(64, 128, 16, 0, 0, 0) == 0
     assert lib.pa_decode_streamk_workers(64, 128, 16, 512, 1, 0) == 0
-    assert lib.pa_decode_streamk_workers(64, 128, 8, 0, 1, 0) == 0
+    # block size 8 takes the stream-K path too (its worker count needs a GPU)
+    assert lib.pa_decode_streamk_workers(64, 128, 8, 0, 1, 0) != 0
     assert lib.pa_decode_streamk_workers(64, 128, 16, 0, 1, 1) == 0
     assert lib.pa_decode_streamk_workers(9000, 128, 16, 0, 1, 0) == 0
     assert lib.pa_decode_streamk_workers(64, 96, 16, 0, 1, 0) == -1

@@ -169,7 +169,7 @@ def test_edge_shapes(shape):
         assert np.isfinite(out).all()
 
 
-# Work splits of the stream-K path (bf16, block size >= 16): many segments
+# Work splits of the stream-K path (bf16): many segments
 # per wave (segment switches inside a wave's pipeline), contexts of one tile,
 # empty contexts between non-empty ones, and one context split over ~150
 # waves whose partials are merged.
@@ -185,6 +185,9 @@ STREAMK_CASES = [
     ("many-short-g16-d64", lambda r: _mixed_ctx(r, 1500), 16, 1, 64, 64),
     ("one-long", lambda r: [20000], 4, 1, 128, 32),
     ("long-and-empty", lambda r: [0, 9000, 0, 0, 1, 17, 5000, 0], 16, 4, 128, 16),
+    # block size 8: each 16-token tile covers two blocks
+    ("many-short-bs8", lambda r: _mixed_ctx(r, 2000), 8, 2, 128, 8),
+    ("one-long-bs8-d64", lambda r: [0, 12345, 9], 4, 1, 64, 8),
 ]
 
 
