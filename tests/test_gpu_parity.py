@@ -206,6 +206,22 @@ def test_streamk_splits(case):
     assert np.isfinite(out).all()
 
 
+@pytest.mark.parametrize("num_seqs", [8192, 8193], ids=["streamk-max-batch", "partition-batch"])
+def test_largest_batches(num_seqs):
+    """The largest batch the stream-K path takes (its tile prefix of S+1
+    ints sits in LDS) and one more, which takes fixed partitions: short
+    mixed contexts (empties included), every output checked against the
+    oracle on a sample of sequences (the rest: finite, zero for empty)."""
+    rng = np.random.default_rng(num_seqs)
+    ctx = _mixed_ctx(rng, num_seqs)
+    wl = W.decode_workload(f"largest batch S={num_seqs}", "bf16", ctx, 8, 2, 128, 16, rng=rng,
+                           seed=(13, num_seqs))
+    pick = sorted(set([0, num_seqs - 1] + [int(x) for x in rng.choice(num_seqs, 120, replace=False)]))
+    out, ref = run_both(wl, seqs=pick, check_pools=False)
+    assert max_abs_err(out, ref) <= TOL["bf16"]
+    assert np.isfinite(out).all() and np.all(out[ctx == 0] == 0.0)
+
+
 def test_single_token_is_exact_value_row():
     """ctx == 1: the output equals the only V row (exact in float32)."""
     rng = np.random.default_rng(3)

@@ -65,9 +65,10 @@ def _custom(rng, pre, chunk, hq, hkv, d, bs):
                               hq, hkv, d, bs, rng=rng)
 
 
-# (prefix lengths, chunk lengths, Hq, Hkv, D, bs): every query-group width
-# 16 / G (G = 1, 2, 4, 6, 8, 16), both head dims, every block size, empty
-# chunks, one-token chunks, chunks starting at position 0, > 64 blocks
+# (prefix lengths, chunk lengths, Hq, Hkv, D, bs): every group size G = 1, 2,
+# 4, 6, 8, 16 (128 / G chunk tokens per workgroup, 128 - 128 % G rows used),
+# both head dims, every block size, empty chunks, one-token chunks, chunks
+# starting at position 0, contexts over 64 blocks, a 2048-token chunk
 EDGE = [
     ([0, 40, 3], [37, 16, 1], 8, 8, 64, 32),
     ([100, 0, 17], [64, 0, 129], 16, 8, 128, 16),
@@ -75,6 +76,7 @@ EDGE = [
     ([31, 2], [50, 19], 12, 2, 128, 16),
     ([0, 1100], [21, 40], 16, 1, 64, 16),
     ([1500, 0], [300, 200], 32, 8, 128, 16),
+    ([2000, 37], [2048, 700], 16, 2, 128, 32),   # a 2048-token chunk over a long prefix
 ]
 
 
