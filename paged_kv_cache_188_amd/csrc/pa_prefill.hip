@@ -44,8 +44,8 @@
 // (zeroed past the context) when they are stored to LDS a step later; the
 // barrier orders LDS only, so the next step's global loads stay in flight
 // across it.  (Measured on MI355X, the chunked-prefill workload of 16
-// sequences x 512-token chunks: 783 us with one wave per 16 query rows and
-// no K/V sharing, 626 us with this layout.)
+// sequences x 512-token chunks: 783 us per call with one wave per 16 query
+// rows and no K/V sharing, 605 us with this layout.)
 // Workgroups are numbered so that those of one (sequence, KV head) run on
 // one XCD (consecutive workgroup ids are dealt round-robin over the 8 XCDs),
 // sharing that XCD's L2 for the K/V they all read; within a sequence the
