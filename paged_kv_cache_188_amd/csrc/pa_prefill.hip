@@ -46,10 +46,15 @@
 // across it.  (Measured on MI355X, the chunked-prefill workload of 16
 // sequences x 512-token chunks: 783 us per call with one wave per 16 query
 // rows and no K/V sharing, 605 us with this layout.)
-// Workgroups are numbered so that those of one (sequence, KV head) run on
-// one XCD (consecutive workgroup ids are dealt round-robin over the 8 XCDs),
-// sharing that XCD's L2 for the K/V they all read; within a sequence the
-// later query tiles (more keys) start first.
+// Scheduling: the work of a (sequence, query tile) pair is its number of key
+// steps, known only from device data.  Each workgroup first ranks all pairs
+// by decreasing work (a bucketed counting sort in LDS, the same in every
+// workgroup) and takes the pair at its own id's rank: workgroups start in id
+// order, so the longest items start first and the short ones fill the end.
+// (Measured: the share of workgroup slots in use over the kernel's life was
+// 0.52 with pairs in sequence order, the long items of late sequences forming
+// the tail, and 0.89 longest first.)  The KV heads of a pair take
+// consecutive ids.
 
 #include <type_traits>
 
@@ -73,7 +78,6 @@ constexpr int kRows = 32 * kWaves;  // rows per workgroup
 constexpr int kStep = 32;           // keys per step
 constexpr float kLazyMax = 8.f;
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kXcds = 8;
 
 // Workgroup barrier that orders LDS only: global loads in flight stay in
 // flight across it (a full __syncthreads would wait for them).
@@ -143,6 +147,91 @@ __device__ __forceinline__ int load_ids(const int32_t* bt, int chunk, int n, int
   return (v >= 0 && v < num_blocks) ? v : 0;
 }
 
+constexpr int kSortMaxPairs = 16384;  // larger grids keep the natural order
+constexpr int kBuckets = 256;
+
+// Key steps of work item pair i = (sequence i / qtiles, query tile i % qtiles):
+// 0 for a pair with no chunk token (its workgroups exit at once), else 1 +
+// the number of 32-key steps its workgroups walk.
+__device__ __forceinline__ int pair_work(const DecodeParams& p, const int32_t* query_start,
+                                         int64_t total_q, int tq, int qtiles, int i) {
+  const int seq = i / qtiles, qt = i % qtiles;
+  const int q0 = query_start[seq];
+  const int L = query_start[seq + 1] - q0;
+  const int j0 = qt * tq;
+  if (q0 < 0 || L < 0 || (int64_t)q0 + L > total_q || j0 >= L) return 0;
+  const int n = min(max(p.context_lens[seq], 0), p.max_tokens);
+  const int last = n - L + j0 + min(tq, L - j0) - 1;
+  return last < 0 ? 1 : last / kStep + 2;
+}
+
+// The pair at position `rank` when the pairs are ordered by decreasing work
+// (bucketed into kBuckets levels, ties in index order): workgroups are
+// dispatched in id order, so the longest work starts first and the short
+// items fill in at the end (longest-processing-time-first).  Every thread of
+// the workgroup takes part and gets the answer; `sm` is kBuckets + kThreads
+// + 4 ints of LDS.
+__device__ int longest_first_pair(const DecodeParams& p, const int32_t* query_start,
+                                  int64_t total_q, int tq, int qtiles, int P, int rank, int* sm) {
+  const int tid = threadIdx.x;
+  int* hist = sm;                   // [kBuckets]
+  int* part = sm + kBuckets;        // [kThreads]
+  int* res = part + kThreads;       // [4]
+  int wmax = 0;
+  for (int i = tid; i < P; i += kThreads)
+    wmax = max(wmax, pair_work(p, query_start, total_q, tq, qtiles, i));
+  part[tid] = wmax;
+  for (int b = tid; b < kBuckets; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  if (tid == 0) {
+    int m = 0;
+    for (int t = 0; t < kThreads; ++t) m = max(m, part[t]);
+    res[0] = m;
+  }
+  __syncthreads();
+  wmax = res[0];
+  auto bucket = [&](int w) {
+    return w == 0 ? 0 : 1 + (int)((int64_t)(w - 1) * (kBuckets - 2) / max(wmax - 1, 1));
+  };
+  for (int i = tid; i < P; i += kThreads)
+    atomicAdd(&hist[bucket(pair_work(p, query_start, total_q, tq, qtiles, i))], 1);
+  __syncthreads();
+  if (tid == 0) {  // the bucket holding `rank`, buckets taken from the top
+    int start = 0, b = kBuckets - 1;
+    for (; b > 0 && start + hist[b] <= rank; --b) start += hist[b];
+    res[1] = b;
+    res[2] = rank - start;  // position inside the bucket
+  }
+  __syncthreads();
+  const int tb = res[1], want = res[2];
+  const int chunk = (P + kThreads - 1) / kThreads;  // contiguous slices keep index order
+  const int lo = min(P, tid * chunk), hi = min(P, lo + chunk);
+  int cnt = 0;
+  for (int i = lo; i < hi; ++i)
+    cnt += bucket(pair_work(p, query_start, total_q, tq, qtiles, i)) == tb;
+  part[tid] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int before = 0, t = 0;
+    for (; t < kThreads - 1 && before + part[t] <= want; ++t) before += part[t];
+    res[1] = t;
+    res[2] = want - before;
+  }
+  __syncthreads();
+  if (tid == res[1]) {
+    int k = res[2];
+    for (int i = lo; i < hi; ++i)
+      if (bucket(pair_work(p, query_start, total_q, tq, qtiles, i)) == tb && k-- == 0) {
+        res[3] = i;
+        break;
+      }
+  }
+  __syncthreads();
+  const int pair = res[3];
+  __syncthreads();  // `sm` is reused by the caller
+  return pair;
+}
+
 template <int D, int BS>
 __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
     const DecodeParams p, const int32_t* __restrict__ query_start, int64_t total_q, int tq,
@@ -160,14 +249,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
 
-  // workgroup -> (sequence, KV head, query tile)
-  const int64_t per_xcd = (n_items + kXcds - 1) / kXcds;
-  const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  // workgroup -> (sequence, query tile) pair, longest work first, and KV head
+  const int64_t item = blockIdx.x;
   if (item >= n_items) return;
-  const int64_t per_seq = (int64_t)p.num_kv_heads * qtiles;
-  const int seq = (int)(item / per_seq);
-  const int kvh = (int)((item % per_seq) / qtiles);
-  const int qt = qtiles - 1 - (int)(item % qtiles);
+  const int P = (int)(n_items / p.num_kv_heads);
+  const int rank = (int)(item / p.num_kv_heads);
+  const int kvh = (int)(item % p.num_kv_heads);
+  const bool sorted = P <= kSortMaxPairs;
+  const int pair = sorted ? longest_first_pair(p, query_start, total_q, tq, qtiles, P, rank,
+                                               reinterpret_cast<int*>(&smem[0][0]))
+                          : rank;
+  const int seq = pair / qtiles;
+  const int qt = sorted ? pair % qtiles : qtiles - 1 - pair % qtiles;  // else: later tiles first
   const int q0 = query_start[seq];
   const int L = query_start[seq + 1] - q0;
   const int j0 = qt * tq;
@@ -395,9 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
 template <int D>
 hipError_t launch_d(const DecodeParams& p, const int32_t* query_start, int64_t total_q, int tq,
                     int qtiles, int64_t items, int block_size, hipStream_t stream) {
-  // padded to a multiple of the XCD count so that the id mapping is a bijection
-  const int64_t blocks = (items + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid((unsigned)blocks), block(kThreads);
+  const dim3 grid((unsigned)items), block(kThreads);
   if (block_size == 16)
     hipLaunchKernelGGL((prefill_flash_kernel<D, 16>), grid, block, 0, stream, p, query_start,
                        total_q, tq, qtiles, items);
