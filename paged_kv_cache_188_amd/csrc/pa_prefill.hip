@@ -37,15 +37,23 @@
 //                 into hi + lo bf16 parts (hi = upper 16 bits, lo = the
 //                 rounded rest), so the weights keep float32 accuracy;
 //                 bf16 x bf16 products are exact and accumulate in float32.
-//                 Output tile nt: lane holds dims (D/16)*col + nt of rows
-//                 4*grp + r (the decode's dim order).
+//                 V's B operand (keys along k) is read from the row-major
+//                 V tile with gfx950's transposing LDS load
+//                 (ds_read_b64_tr_b16); one 16-byte pad per V row spreads
+//                 the 16 rows such a load touches over all LDS banks.
+//                 Output tile nt: lane holds dim 16*nt + col of rows
+//                 4*grp + r.
 // Latency: the block ids of 64 blocks are fetched at once (one per lane),
-// so no K/V load waits for a table lookup; loaded V rows are only inspected
-// (zeroed past the context) when they are stored to LDS a step later; the
-// barrier orders LDS only, so the next step's global loads stay in flight
-// across it.  (Measured on MI355X, the chunked-prefill workload of 16
-// sequences x 512-token chunks: 783 us per call with one wave per 16 query
-// rows and no K/V sharing, 605 us with this layout.)
+// so no K/V load waits for a table lookup; K/V addresses are a uniform
+// block base plus a per-lane 32-bit offset fixed for the whole walk; V rows
+// past the context are zeroed only on the step that reaches past it, when
+// they are stored to LDS; the barrier orders LDS only, so the next step's
+// global loads stay in flight across it.  (Measured on MI355X, the
+// chunked-prefill workload of 16 sequences x 512-token chunks: 783 us per
+// call with one wave per 16 query rows and no K/V sharing, 605 us with this
+// layout; the vector-ALU trims -- uniform base addresses, three-way max, V
+// zeroing on one step, transposing V loads instead of byte permutes -- took
+// a further 17 %.)
 // Scheduling: the work of a (sequence, query tile) pair is its number of key
 // steps, known only from device data.  Each workgroup first ranks all pairs
 // by decreasing work (a bucketed counting sort in LDS, the same in every
@@ -55,8 +63,6 @@
 // 0.52 with pairs in sequence order, the long items of late sequences forming
 // the tail, and 0.89 longest first.)  The KV heads of a pair take
 // consecutive ids.
-
-#include <type_traits>
 
 #include "pa_internal.h"
 
@@ -71,6 +77,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // registers
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
@@ -86,9 +93,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-
-template <int D>
-using VPiece = typename std::conditional<D == 128, u32x4_t, u32x2_t>::type;  // D/16 bf16
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -116,25 +120,34 @@ __device__ __forceinline__ void split_weights(const float (&p)[8], bf16x8_t& hi,
 
 // Global -> register loads of one 16-key half for thread u (0..127) of the
 // half: K chunk c = u + 128 i is granule c / 16 of key c % 16, V chunk c is
-// granule c % (D/8) of key c / (D/8); key0 is the half's first position and
-// phys its physical block.  Every address is inside the pools; V rows past
-// the context are zeroed when stored to LDS (not here: a select on the
-// loaded value would wait for the load).
+// granule c % (D/8) of key c / (D/8); koff / voff hold the chunks' byte
+// offsets inside a block's 16 keys, so an address is the (wave-uniform)
+// base of (phys, kvh, key0 % BS) plus a 32-bit lane offset.  key0 is the
+// half's first position and phys its physical block.  Every address is
+// inside the pools; V rows past the context are zeroed when stored to LDS
+// (not here: a select on the loaded value would wait for the load).
 template <int D, int BS>
 __device__ __forceinline__ void load_step(const uint16_t* kpool, const uint16_t* vpool, int phys,
-                                          int n, int hkv, int kvh, int key0, int u,
+                                          int hkv, int kvh, int key0,
+                                          const uint32_t (&koff)[D / 64],
+                                          const uint32_t (&voff)[D / 64],
                                           u32x4_t (&kreg)[D / 64], u32x4_t (&vreg)[D / 64]) {
-  constexpr int GR = D / 8;
   const int o = key0 % BS;
   const int64_t cb = ((int64_t)phys * hkv + kvh) * ((int64_t)BS * D);
+  const char* kb = reinterpret_cast<const char*>(kpool + cb + o * 8);
+  const char* vb = reinterpret_cast<const char*>(vpool + cb + (int64_t)o * D);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
-    const int c = u + 128 * i;
-    kreg[i] = *reinterpret_cast<const u32x4_t*>(kpool + cb +
-                                                ((int64_t)(c >> 4) * BS + o + (c & 15)) * 8);
-    vreg[i] = *reinterpret_cast<const u32x4_t*>(vpool + cb + (int64_t)(o + c / GR) * D +
-                                                (c % GR) * 8);
+    kreg[i] = *reinterpret_cast<const u32x4_t*>(kb + (size_t)koff[i]);
+    vreg[i] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)voff[i]);
   }
+}
+
+// max of three (v_max3_f32; fmaxf would first quiet each MFMA result)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // Physical block ids of logical blocks 64*chunk .. 64*chunk + 63, one per
@@ -242,8 +255,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
   constexpr int GR = D / 8;    // 16-byte granules per row
   constexpr int HALF = 2 * D;  // 16-byte chunks of K (or V) per 16-key half
   constexpr int CH = D / 64;   // chunks per thread per half, K and V each
-  // [buffer][K: half, granule, key | V: half, key, granule] in 16-byte units
-  __shared__ u32x4_t smem[2][4 * HALF];
+  constexpr int VRS = GR + 1;   // V row stride in 16-byte units: one unit of padding
+  // [buffer][K: half, granule, key | V: key, granule (+ pad)] in 16-byte units
+  __shared__ u32x4_t smem[2][2 * HALF + kStep * VRS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -315,6 +329,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
   const uint16_t* vpool = static_cast<const uint16_t*>(p.v_cache);
   const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
   u32x4_t kreg[CH], vreg[CH];
+  uint32_t koff[CH], voff[CH];  // byte offsets of this thread's chunks in a 16-key half
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = u + 128 * i;
+    koff[i] = (uint32_t)(((c >> 4) * BS + (c & 15)) * 16);
+    voff[i] = (uint32_t)((c / GR) * D * 2 + (c % GR) * 16);
+  }
   // block ids come 64 at a time, one per lane, and are picked with readlane:
   // the K/V loads of a step never wait for a table lookup
   int ids = 0, ids_chunk = -1;
@@ -325,9 +346,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
       ids_chunk = blk / 64;
       ids = load_ids<BS>(bt, ids_chunk, n, p.num_blocks, lane);
     }
-    load_step<D, BS>(kpool, vpool, __builtin_amdgcn_readlane(ids, blk % 64), n,
-                     p.num_kv_heads, kvh, key0, u, kreg, vreg);
+    load_step<D, BS>(kpool, vpool, __builtin_amdgcn_readlane(ids, blk % 64), p.num_kv_heads, kvh,
+                     key0, koff, voff, kreg, vreg);
   };
+  // byte offset of this lane's transposing-load source in the V tile (key
+  // 4*grp + col/4, dims 4*(col%4) .. +3 of dim tile 0)
+  const int vlane = (4 * grp + (col >> 2)) * VRS * 16 + (col & 3) * 8;
   f32x4_t acc[2][DV];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -339,12 +363,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
   for (int step = 0; step < nsteps; ++step) {
     u32x4_t* buf = smem[step & 1];
     const int skey0 = step * kStep + th * 16;  // first key of this thread's half
+    if (skey0 + 16 > n) {  // keys past the context: V rows zeroed (wave-uniform test)
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = u + 128 * i;
+        if (skey0 + c / (D / 8) >= n) vreg[i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = u + 128 * i;
       buf[th * HALF + c] = kreg[i];
-      buf[2 * HALF + th * HALF + c] =
-          skey0 + c / (D / 8) < n ? vreg[i] : u32x4_t{0u, 0u, 0u, 0u};  // keys past the context
+      buf[2 * HALF + (th * 16 + c / GR) * VRS + c % GR] = vreg[i];
     }
     lds_barrier();
     if (step + 1 < nsteps) fetch(step + 1);
@@ -371,14 +401,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
           for (int h = 0; h < 2; ++h)
             sc[kh][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kh][s], qv[h][s], sc[kh][h], 0, 0, 0);
     }
-    // V rows 4*grp + j of each half, dims (D/16)*col .. +D/16-1
-    const VPiece<D>* vb = reinterpret_cast<const VPiece<D>*>(buf + 2 * HALF);
-    VPiece<D> vr[2][4];
+    // B operands of P V, read before the softmax so the loads overlap it.
+    // Dim tile nt: lane (grp, n) holds V at keys 4*grp + j and 16 + 4*grp + j
+    // (j = 0..3; the order of P's elements) and dim 16*nt + n, read with two
+    // transposing LDS loads: source lane 4*j + r of a 16-lane group supplies
+    // key 4*grp + j (+16), dims 16*nt + 4*r .. +3
+    bf16x8_t bv[DV];
+    {
+      const char* vl = reinterpret_cast<const char*>(buf + 2 * HALF) + vlane;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vr[kh][j] = vb[(kh * 16 + 4 * grp + j) * 16 + col];
-
+      for (int nt = 0; nt < DV; ++nt) {
+        const v4s_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(vl + nt * 32));
+        const v4s_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(vl + 16 * VRS * 16 + nt * 32));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo4), h2 = __builtin_bit_cast(u32x2_t, hi4);
+        bv[nt] = as_bf16x8(u32x4_t{l2.x, l2.y, h2.x, h2.y});
+      }
+    }
     // softmax: exponent arguments s * c - m (the causal mask only on steps
     // that reach past some row's position), lazy reference point, P split
     const bool diag = step * kStep + kStep - 1 > wmin;
@@ -401,8 +441,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
     float lmax[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      lmax[h] = fmaxf(fmaxf(fmaxf(x[h][0], x[h][1]), fmaxf(x[h][2], x[h][3])),
-                      fmaxf(fmaxf(x[h][4], x[h][5]), fmaxf(x[h][6], x[h][7]))) * c;
+      lmax[h] = max3f(max3f(x[h][0], x[h][1], x[h][2]), max3f(x[h][3], x[h][4], x[h][5]),
+                      max3f(x[h][6], x[h][7], x[h][7])) * c;
     if (__any(lmax[0] > m_run[0] + kLazyMax || lmax[1] > m_run[1] + kLazyMax)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -433,34 +473,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
     // accumulator
 #pragma unroll
     for (int n0 = 0; n0 < DV; n0 += 4) {
-      bf16x8_t bv[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int nt = n0 + t;
-        const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
-        const int w = nt >> 1;
-        u32x4_t bw;
-        bw.x = __builtin_amdgcn_perm(vr[0][1][w], vr[0][0][w], sel);
-        bw.y = __builtin_amdgcn_perm(vr[0][3][w], vr[0][2][w], sel);
-        bw.z = __builtin_amdgcn_perm(vr[1][1][w], vr[1][0][w], sel);
-        bw.w = __builtin_amdgcn_perm(vr[1][3][w], vr[1][2][w], sel);
-        bv[t] = as_bf16x8(bw);
-      }
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          acc[h][n0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[h], bv[t], acc[h][n0 + t], 0, 0, 0);
+          acc[h][n0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[h], bv[n0 + t], acc[h][n0 + t], 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          acc[h][n0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[h], bv[t], acc[h][n0 + t], 0, 0, 0);
+          acc[h][n0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[h], bv[n0 + t], acc[h][n0 + t], 0, 0, 0);
     }
   }
 
   // normalise and store: acc[h][nt][r] is row wave*32 + 16h + 4*grp + r,
-  // dim (D/16)*col + nt
+  // dim 16*nt + col
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float l = l_run[h];
@@ -475,12 +502,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
       // a row that sees a key has l >= 1 (its largest weight is >= 1)
       const float inv = base + tk >= 0 ? 1.0f / l_c : 0.f;
       float* dst = p.out + ((int64_t)(q0 + j0 + tk) * p.num_q_heads + (int64_t)kvh * G + hd) * D +
-                   DV * col;
+                   col;
 #pragma unroll
-      for (int k = 0; k < DV; k += 4)
-        *reinterpret_cast<float4*>(dst + k) =
-            make_float4(acc[h][k][r] * inv, acc[h][k + 1][r] * inv, acc[h][k + 2][r] * inv,
-                        acc[h][k + 3][r] * inv);
+      for (int nt = 0; nt < DV; ++nt) dst[16 * nt] = acc[h][nt][r] * inv;
     }
   }
 }
