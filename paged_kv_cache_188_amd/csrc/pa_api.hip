@@ -423,11 +423,11 @@ pa_status pa_prefill_attention(float* out, const void* q, const void* k_cache,
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  {  // 256 threads per workgroup, workgroups padded to a multiple of 8:
-     // at most 2^32 - 1 work-items in the launch
+  {  // one workgroup per (sequence, KV head, query tile): at most 2^32 - 1
+     // work-items in the launch
     const int32_t tq = pa::prefill_tokens_per_workgroup(num_q_heads / num_kv_heads);
     const int64_t items = (int64_t)num_seqs * num_kv_heads * ((max_query_len + tq - 1) / tq);
-    if ((items + 7) / 8 * 8 * 256 > UINT32_MAX) return PA_ERR_SHAPE;
+    if (items * pa::prefill_threads_per_workgroup() > UINT32_MAX) return PA_ERR_SHAPE;
   }
   if (num_seqs == 0 || num_q_tokens == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)

@@ -100,6 +100,7 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, pa
 // workgroup per (sequence, KV head, prefill_tokens_per_workgroup(G) chunk
 // tokens).
 int prefill_tokens_per_workgroup(int group);
+int prefill_threads_per_workgroup();
 hipError_t launch_prefill(const DecodeParams& p, const int32_t* query_start, int64_t total_q,
                           int max_query_len, int head_dim, int block_size, hipStream_t stream);
 

@@ -528,6 +528,7 @@ hipError_t launch_d(const DecodeParams& p, const int32_t* query_start, int64_t t
 }  // namespace
 
 int prefill_tokens_per_workgroup(int group) { return kRows / group; }
+int prefill_threads_per_workgroup() { return kThreads; }
 
 hipError_t launch_prefill(const DecodeParams& p, const int32_t* query_start, int64_t total_q,
                           int max_query_len, int head_dim, int block_size, hipStream_t stream) {
