@@ -134,3 +134,15 @@ def test_prefill_placement_invariance_bitwise():
         _, out = _run(w)
         outs.append(out)
     assert outs[0].tobytes() == outs[1].tobytes() == outs[2].tobytes()
+
+
+def test_prefill_more_pairs_than_the_sort_takes():
+    """16400 one-token chunks: more (sequence, query tile) pairs than the
+    kernel's in-LDS longest-first ranking handles (16384), so the workgroups
+    take the pairs in index order -- the results are the same."""
+    rng = np.random.default_rng(11)
+    S = 16400
+    wl = W.prefill_workload("prefill 16400 one-token chunks", W.BF16, rng.integers(0, 40, size=S),
+                            np.ones(S, np.int64), 8, 8, 64, 16, rng=rng)
+    dev, out = _run(wl)
+    _check(wl, dev, out)
