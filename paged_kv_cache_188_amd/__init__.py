@@ -296,14 +296,41 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
                                               PA_DECODE_VECTOR_ONLY if vector_only else 0))
 
 
+class PreparedCall:
+    """One library call whose arguments were validated and marshalled once.
+
+    Calling it issues the same launch(es) again on the same stream, with the
+    same device buffers (their contents may change between calls): the
+    per-call host work is one foreign-function call.  The tensors the call
+    reads and writes are kept alive by the object.  ``result`` is what the
+    unprepared call returns (the output tensor)."""
+
+    __slots__ = ("_fn", "_name", "_args", "_keep", "result")
+
+    def __init__(self, name, args, keep, result):
+        self._fn = getattr(lib(), name)
+        self._name = name
+        self._args = tuple(args)
+        self._keep = keep
+        self.result = result
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code != 0:
+            raise PAError(self._name, code)
+        return self.result
+
+
 def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                      partition_size=0, workspace=None, out=None, vector_only=False, stream=None,
-                     k_new=None, v_new=None):
+                     k_new=None, v_new=None, prepare=False):
     """Paged decode attention; returns float32 [S][Hq][D].  ``workspace`` (a
     uint8 device tensor) is allocated here when not given.  With ``k_new`` /
     ``v_new`` ([S][Hkv][D]) each sequence's new token (position ctx-1) is
     stored in the pools and attended in the same call
-    (pa_decode_attention_append)."""
+    (pa_decode_attention_append).  With ``prepare=True`` nothing is launched:
+    the validated call is returned as a PreparedCall, to be issued later (as
+    often as wanted) with the same buffers."""
     import torch
     s, hq, d = q.shape
     nb, hkv, bs, d2 = _pools(k_cache, v_cache)
@@ -320,6 +347,10 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max
     if out is None:
         out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
+    ws = (_ptr(workspace) if workspace is not None else None,
+          workspace.numel() if workspace is not None else 0)
+    tail = (_dtype_code(k_cache), PA_DECODE_VECTOR_ONLY if vector_only else 0, _stream(stream))
+    keep = (q, k_cache, v_cache, block_tables, context_lens, workspace, out, k_new, v_new)
     if k_new is not None:
         if v_new is None or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
             raise TypeError("k_new and v_new must both be given, with the pool's element type")
@@ -327,21 +358,17 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max
             raise ValueError("k_new/v_new must be [S][Hkv][D]")
         if k_new.stride(2) != 1 or k_new.stride(1) != d or v_new.stride() != k_new.stride():
             raise ValueError("k_new/v_new rows must be contiguous [Hkv][D] with one token stride")
-        _check("pa_decode_attention_append", lib().pa_decode_attention_append(
-            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
-            k_new.stride(0), _ptr(block_tables), _ptr(context_lens), s, hq, hkv, d, bs, nb, mb,
-            int(max_context_len), float(scale), int(partition_size),
-            _ptr(workspace) if workspace is not None else None,
-            workspace.numel() if workspace is not None else 0, _dtype_code(k_cache),
-            PA_DECODE_VECTOR_ONLY if vector_only else 0, _stream(stream)))
-        return out
-    _check("pa_decode_attention", lib().pa_decode_attention(
-        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-        _ptr(context_lens), s, hq, hkv, d, bs, nb, mb, int(max_context_len), float(scale),
-        int(partition_size), _ptr(workspace) if workspace is not None else None,
-        workspace.numel() if workspace is not None else 0, _dtype_code(k_cache),
-        PA_DECODE_VECTOR_ONLY if vector_only else 0, _stream(stream)))
-    return out
+        name = "pa_decode_attention_append"
+        args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                k_new.stride(0), _ptr(block_tables), _ptr(context_lens), s, hq, hkv, d, bs, nb,
+                mb, int(max_context_len), float(scale), int(partition_size)) + ws + tail
+    else:
+        name = "pa_decode_attention"
+        args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                _ptr(context_lens), s, hq, hkv, d, bs, nb, mb, int(max_context_len),
+                float(scale), int(partition_size)) + ws + tail
+    call = PreparedCall(name, args, keep, out)
+    return call if prepare else call()
 
 
 def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,

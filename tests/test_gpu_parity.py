@@ -288,6 +288,37 @@ def test_run_to_run_determinism():
     assert a.tobytes() == b.tobytes() == c.tobytes()
 
 
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_prepared_call_equals_direct_call_bitwise(cid):
+    """A PreparedCall (arguments marshalled once, issued several times) runs
+    the same launches as the direct call: equal outputs and pools, bit for
+    bit, and every re-issue gives the same answer."""
+    wl = W.make(cid, small=(cid != 1))
+    DeviceWorkload = _device()
+    res = []
+    for prepared in (False, True):
+        dev = DeviceWorkload(wl)
+        dev.run_setup()
+        if prepared:
+            ops = dev.step_ops_append
+            calls = dev.prepare(ops)
+            outs = []
+            for _ in range(2):
+                for c in calls:
+                    c()
+                outs.append(dev.out.cpu().numpy())
+            assert outs[0].tobytes() == outs[1].tobytes()
+            o = outs[0]
+        else:
+            o = dev.run_step(append=True).cpu().numpy()
+            o2 = dev.run_step(append=True).cpu().numpy()
+            assert o.tobytes() == o2.tobytes()
+        res.append((o, dev.pool_bits()))
+    assert res[0][0].tobytes() == res[1][0].tobytes()
+    assert res[0][1][0].tobytes() == res[1][1][0].tobytes()
+    assert res[0][1][1].tobytes() == res[1][1][1].tobytes()
+
+
 def test_workspace_reuse_with_new_queries():
     """Consecutive calls on one workspace: partials and arrival counters left
     by a call never leak into the next (new queries give the oracle's new

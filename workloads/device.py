@@ -154,6 +154,29 @@ class DeviceWorkload:
                                     vector_only=vector_only, stream=stream)
         return self.out
 
+    def prepare(self, ops, pool=0, partition_size=None, stream=None):
+        """Zero-argument callables that issue `ops` on pool copy `pool`, as
+        _run does with record_slots=False; the decode calls are validated and
+        marshalled here once (pa.PreparedCall), so issuing one costs a single
+        foreign-function call."""
+        wl = self.wl
+        k, v = self.pools[pool]
+        part = wl.partition_size if partition_size is None else partition_size
+        calls = []
+        for op in ops:
+            kind, x = op
+            if kind in ("decode", "decode_append"):
+                table = x["table"] if kind == "decode_append" else x
+                kw = dict(k_new=x["k"], v_new=x["v"]) if kind == "decode_append" else {}
+                calls.append(pa.decode_attention(
+                    self.q, k, v, self.tables[table], self.ctx, wl.scale, self.max_ctx,
+                    partition_size=part, workspace=self._ensure_workspace(part, False),
+                    out=self.out, stream=stream, prepare=True, **kw))
+            else:
+                calls.append(lambda op=op: self._run([op], pool, partition_size=part,
+                                                     stream=stream, record_slots=False))
+        return calls
+
     def run_setup(self, pool=0, **kw):
         self._run(self.setup_ops, pool, **kw)
 
