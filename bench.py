@@ -14,8 +14,12 @@ step is served from a cache warmed by the previous one.
     python bench.py [--steps K] [--warmup W] [--config 2]
 
 prints ONE JSON line: KV GB/s of the whole step (`value`), seq-steps/s,
-the decode kernel's roofline fraction (HIP events around every decode
-launch on the stream it runs on) and the CPU oracle's rate on a bounded sample.
+the decode call's roofline fraction (HIP events on the stream it runs on:
+one pair around the timed back-to-back steps when a step is the decode call
+alone, else a pair around each call), the median / p10 / p90 of single
+calls, the achievable rates of the bandwidth probes (a contiguous stream and
+the decode's own K/V gather with no arithmetic; --no-probes skips them) and
+the CPU oracle's rate on a bounded sample.
 
     python bench.py --workload prefill
 
@@ -62,6 +66,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's timed CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the bandwidth probes (achievable stream / gather rates)")
     ap.add_argument("--partition", type=int, default=None,
                     help="decode partition size (default: the workload's / the library's choice)")
     ap.add_argument("--separate", action="store_true",
@@ -328,6 +334,55 @@ def calibrate_copy(steps):
                       "write_bytes_per_launch": 2 * half * block_bytes}), flush=True)
 
 
+def _span_ms(torch, stream, fn, reps):
+    """Average time of fn(r) for r = 0 .. reps-1 issued back to back: one HIP
+    event pair around all of them on `stream`, divided by reps."""
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for r in range(reps):
+        fn(r)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def achievable(torch, pa, dev, wl, npools, stream, reps=20):
+    """What the memory system delivers on this machine with no arithmetic at all
+    (include/pa_probe.h): a contiguous stream over the pools, and the decode
+    call's own K/V chunk gather through the same tables, each at four grid
+    sizes; the best of each is the achievable reference."""
+    table = dev.tables[[x for kind, x in wl.step if kind == "decode"][0]]
+    chunk = wl.block_size * wl.head_dim * (2 if wl.dtype == "bf16" else 4)
+    blocks = int(sum(-(-int(c) // wl.block_size) for c in wl.context_lens if c > 0))
+    gather_bytes = 2 * blocks * wl.num_kv_heads * chunk
+    pool_bytes = sum(t.numel() * t.element_size() for t in dev.pools[0])
+    res = {"gather_bytes": gather_bytes, "stream_bytes": pool_bytes, "grids": {}}
+    best_g = best_s = 0.0
+    for sink_len in (512, 1024, 2048, 4096):
+        def g(r):
+            k, v = dev.pools[r % npools]
+            pa.probe_gather(k, v, table, dev.ctx, sink_len=sink_len, stream=stream)
+
+        def s(r):
+            for t in dev.pools[r % npools]:
+                pa.probe_read(t, sink_len=sink_len, stream=stream)
+        g(0), s(0)
+        tg = _span_ms(torch, stream, g, reps)
+        ts = _span_ms(torch, stream, s, reps)
+        gg, sg = gather_bytes / (tg * 1e-3) / 1e9, pool_bytes / (ts * 1e-3) / 1e9
+        res["grids"][sink_len] = {"gather_gbps": round(gg, 1), "stream_gbps": round(sg, 1)}
+        best_g, best_s = max(best_g, gg), max(best_s, sg)
+    res["gather_gbps"] = round(best_g, 1)
+    res["stream_gbps"] = round(best_s, 1)
+    return res
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -406,6 +461,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # distribution of single calls: every call between its own event pair
+    # (the event packets add their own few microseconds to each)
+    if per_call_events:
+        one_ms = [a.elapsed_time(b) for a, b in events]
+    else:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for k in range(args.steps):
+            step(args.warmup + args.steps + k, evs[k])
+        torch.cuda.synchronize()
+        one_ms = [a.elapsed_time(b) for a, b in evs]
+    ach = None if args.no_probes else achievable(torch, pa, dev, wl, npools, stream)
+
     ms_step = wall * 1e3 / args.steps
     workers = pa.decode_streamk_workers(wl.num_seqs, wl.head_dim, wl.block_size,
                                         wl.partition_size, dev.torch_dtype)
@@ -470,6 +538,10 @@ def main():
         "kv_bytes_per_step": kv_bytes,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_ms": dec_timing,
+        "decode_call_us": {"median": round(1e3 * _pct(one_ms, 0.5), 2),
+                           "p10": round(1e3 * _pct(one_ms, 0.1), 2),
+                           "p90": round(1e3 * _pct(one_ms, 0.9), 2),
+                           "how": "HIP events around each single call"},
         "roofline": {
             "kernel": kernel,
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
@@ -479,6 +551,13 @@ def main():
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
         },
     }
+    if ach is not None:
+        ach["decode_frac_of_gather"] = round(achieved / ach["gather_gbps"], 4)
+        ach["decode_frac_of_stream"] = round(achieved / ach["stream_gbps"], 4)
+        res["achievable"] = ach
+    tr = res["roofline"]["traffic"]
+    if tr:
+        res["roofline"]["traffic_gbps"] = round(tr / (dec_avg_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -58,6 +58,9 @@ SIGNATURES = {
     "pa_bm_tables": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
     "pa_bm_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(BMStats)]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_probe_read": (ctypes.c_int, [_P, _I64, _P, _I32, _P]),
+    "pa_probe_gather": (ctypes.c_int, [_P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
+                                       ctypes.c_int, _P, _I32, _P]),
     "pa_compute_slots": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _P]),
     "pa_write_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32,
                                    ctypes.c_int, _P]),
@@ -397,6 +400,37 @@ def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_sta
         _ptr(context_lens), _ptr(query_start), s, t, hq, hkv, d, bs, nb, block_tables.shape[1],
         int(max_query_len), float(scale), _dtype_code(k_cache), _stream(stream)))
     return out
+
+
+def probe_read(buf, sink_len=2048, stream=None):
+    """Bandwidth probe (include/pa_probe.h): read every byte of the device
+    tensor ``buf`` once with sink_len workgroups; returns the uint32 sink
+    (as int32), whose XOR is the XOR of all 32-bit words of ``buf``."""
+    import torch
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous device tensor")
+    sink = torch.empty(sink_len, dtype=torch.int32, device=buf.device)
+    _check("pa_probe_read", lib().pa_probe_read(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink_len, _stream(stream)))
+    return sink
+
+
+def probe_gather(k_cache, v_cache, block_tables, context_lens, sink_len=2048, stream=None):
+    """Bandwidth probe (include/pa_probe.h): read the K/V chunks a decode
+    call over the same pools, tables and context lengths reads, and nothing
+    else; returns the uint32 sink (as int32)."""
+    import torch
+    nb, hkv, bs, d = _pools(k_cache, v_cache)
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    s, mb = block_tables.shape
+    if context_lens.shape != (s,):
+        raise ValueError("context_lens must be [S] for block_tables [S][MB]")
+    sink = torch.empty(sink_len, dtype=torch.int32, device=k_cache.device)
+    _check("pa_probe_gather", lib().pa_probe_gather(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), mb, _ptr(context_lens), s, hkv, d, bs,
+        nb, _dtype_code(k_cache), _ptr(sink), sink_len, _stream(stream)))
+    return sink
 
 
 class BlockManager:

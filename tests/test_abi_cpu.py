@@ -14,7 +14,8 @@ import pytest
 import paged_kv_cache_188_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_block_manager.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_block_manager.h",
+                                                                "pa_probe.h")]
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced
 MISALIGNED = ctypes.c_void_p(0x10008)
@@ -256,3 +257,35 @@ def test_binding_refuses_to_run_without_the_library(tmp_path, monkeypatch):
     monkeypatch.setattr(pa, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         pa.lib()
+
+
+def test_probe_validation(lib):
+    """The bandwidth probes reject bad scalars before any HIP call."""
+    rd = lambda **k: lib.pa_probe_read(k.get("buf", FAKE), k.get("n", 1 << 20),
+                                       k.get("sink", FAKE), k.get("sink_len", 64), NULL)
+    assert rd(n=-16) == SHAPE
+    assert rd(n=24) == SHAPE                                # not whole 16-byte granules
+    assert rd(sink_len=0) == SHAPE
+    assert rd(sink_len=65537) == SHAPE
+    assert rd(buf=NULL) == NUL
+    assert rd(sink=NULL) == NUL
+    assert rd(buf=MISALIGNED) == UNSUP
+    assert rd(n=0, buf=NULL, sink=NULL) == OK               # nothing to read: no launch
+    ga = lambda **k: lib.pa_probe_gather(
+        k.get("k", FAKE), FAKE, k.get("bt", FAKE), 4, FAKE, k.get("S", 2), 2, k.get("D", 128),
+        k.get("bs", 16), 10, k.get("dtype", 1), k.get("sink", FAKE), k.get("sink_len", 64), NULL)
+    assert ga(dtype=5) == DTYPE
+    assert ga(D=96) == UNSUP
+    assert ga(bs=12) == UNSUP
+    assert ga(S=-1) == SHAPE
+    assert ga(sink_len=0) == SHAPE
+    assert ga(k=NULL) == NUL
+    assert ga(bt=NULL) == NUL
+    assert ga(sink=NULL) == NUL
+    assert ga(k=MISALIGNED) == UNSUP
+    assert ga(S=0, k=NULL, sink=NULL) == OK
+
+
+def test_probe_gather_batch_limit(lib):
+    assert lib.pa_probe_gather(FAKE, FAKE, FAKE, 4, FAKE, 16385, 2, 128, 16, 10, 1, FAKE, 64,
+                               NULL) == UNSUP
