@@ -296,22 +296,22 @@ def swap_main(args):
 
 
 def measured_traffic(wl):
-    """HBM bytes per decode call from the committed counter summary, if it was
-    taken on this workload with the decode source as it is now (else None)."""
+    """HBM bytes per decode call from a committed counter summary
+    (profiles/decode_traffic*.txt) taken on this workload with the decode
+    source as it is now, if there is one (else None)."""
+    import glob
     import hashlib
     src = os.path.join(ROOT, "paged_kv_cache_188_amd", "csrc", "pa_decode.hip")
-    path = os.path.join(ROOT, "profiles", "decode_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != sha or kv.get("workload") != wl.name:
-        return None
-    return int(kv["traffic_bytes_per_launch"])
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "decode_traffic*.txt"))):
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") == sha and kv.get("workload") == wl.name:
+            return int(kv["traffic_bytes_per_launch"])
+    return None
 
 
 def calibrate_copy(steps):
