@@ -109,8 +109,24 @@ def cpu_baseline(wl, budget_s):
     wall = time.perf_counter() - t0
     r1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
+    # the step's other operations, each once, as the oracle does them (slot
+    # computation + write of the new tokens; the copy-on-write copies)
+    others = {}
+    for kind, x in wl.step:
+        t1 = time.perf_counter()
+        if kind == "write":
+            sl = O.slot_mapping(wl.tables[x.table], x.seq_ids, x.positions, wl.block_size,
+                                wl.num_blocks)
+            O.write_kv(kp, vp, x.k, x.v, sl)
+            others["write"] = {"ms": round(1e3 * (time.perf_counter() - t1), 3),
+                               "tokens": int(x.positions.size)}
+        elif kind == "copy":
+            O.copy_blocks(kp, vp, x)
+            others["copy"] = {"ms": round(1e3 * (time.perf_counter() - t1), 3),
+                              "pairs": int(len(x))}
     return {
         "value": kv / wall / 1e9, "unit": "GB/s", "cores": round(cpu / wall, 2), "kind": "oracle",
+        "other_ops_once": others,
         "sample": (f"float64 numpy oracle decode, one sequence (all {wl.num_q_heads} query heads) "
                    f"per call, {done} sequence-steps cycling over the {wl.num_seqs} sequences of "
                    f"the same workload ({done / wl.num_seqs:.2f} passes): {wall:.1f} s wall, "
@@ -383,6 +399,33 @@ def achievable(torch, pa, dev, wl, npools, stream, reps=20):
     return res
 
 
+def other_ops_timing(torch, dev, wl, npools, stream, reps=20):
+    """The step's KV write (pa_write_kv_at of its new tokens, the same rows
+    the append call stores) and copy-on-write copies (pa_copy_blocks), each
+    timed alone: one event pair around reps back-to-back calls.  Bytes are
+    the K/V rows or blocks read plus written."""
+    e = 2 if wl.dtype == "bf16" else 4
+    res = {}
+    for op in dev.step_ops:
+        kind, x = op
+        if kind not in ("write", "copy"):
+            continue
+        calls = [dev.prepare([op], k, stream=stream)[0] for k in range(npools)]
+        calls[0]()
+        ms = _span_ms(torch, stream, lambda r: calls[r % npools](), reps)
+        if kind == "write":
+            t = int(x["positions"].numel())
+            nbytes = 2 * 2 * t * wl.num_kv_heads * wl.head_dim * e + 20 * t
+            res["pa_write_kv_at"] = {"us": round(ms * 1e3, 2), "tokens": t,
+                                     "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        else:
+            n = int(x.shape[0])
+            nbytes = 2 * 2 * n * wl.num_kv_heads * wl.block_size * wl.head_dim * e + 8 * n
+            res["pa_copy_blocks"] = {"us": round(ms * 1e3, 2), "pairs": n,
+                                     "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    return res
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -473,6 +516,7 @@ def main():
         torch.cuda.synchronize()
         one_ms = [a.elapsed_time(b) for a, b in evs]
     ach = None if args.no_probes else achievable(torch, pa, dev, wl, npools, stream)
+    ops_timing = other_ops_timing(torch, dev, wl, npools, stream)
 
     ms_step = wall * 1e3 / args.steps
     workers = pa.decode_streamk_workers(wl.num_seqs, wl.head_dim, wl.block_size,
@@ -551,6 +595,18 @@ def main():
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
         },
     }
+    res["other_ops"] = ops_timing
+    uniq = wl.unique_kv_bytes()
+    if uniq < kv_bytes:
+        # blocks shared between sequences: the call reads each sequence's
+        # whole context through its table, and the repeated reads of shared
+        # blocks can hit in the caches, so the logical-byte rate above is not
+        # a fraction of HBM traffic; the distinct blocks' bytes are the least
+        # the HBM must deliver
+        res["roofline"]["note"] = ("logical bytes (each sequence's full context); shared "
+                                   "blocks may be served from cache")
+        res["roofline"]["unique_kv_bytes"] = uniq
+        res["roofline"]["unique_kv_gbps"] = round(uniq / (dec_avg_ms * 1e-3) / 1e9, 1)
     if ach is not None:
         ach["decode_frac_of_gather"] = round(achieved / ach["gather_gbps"], 4)
         ach["decode_frac_of_stream"] = round(achieved / ach["stream_gbps"], 4)

@@ -163,6 +163,31 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be contiguous")
 
 
+class PreparedCall:
+    """One library call whose arguments were validated and marshalled once.
+
+    Calling it issues the same launch(es) again on the same stream, with the
+    same device buffers (their contents may change between calls): the
+    per-call host work is one foreign-function call.  The tensors the call
+    reads and writes are kept alive by the object.  ``result`` is what the
+    unprepared call returns (the output tensor)."""
+
+    __slots__ = ("_fn", "_name", "_args", "_keep", "result")
+
+    def __init__(self, name, args, keep, result):
+        self._fn = getattr(lib(), name)
+        self._name = name
+        self._args = tuple(args)
+        self._keep = keep
+        self.result = result
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code != 0:
+            raise PAError(self._name, code)
+        return self.result
+
+
 # ---------------------------------------------------------------------------
 # operations
 # ---------------------------------------------------------------------------
@@ -205,10 +230,11 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
 
 
 def write_kv_at(k_cache, v_cache, k_new, v_new, block_tables, positions, seq_ids=None,
-                slots_out=None, stream=None):
+                slots_out=None, stream=None, prepare=False):
     """compute_slots + write_kv in one launch: token j goes to the slot of
     (seq_ids[j] or j, positions[j]); the slots are also written to
-    ``slots_out`` when given."""
+    ``slots_out`` when given.  With ``prepare=True`` the validated call is
+    returned as a PreparedCall instead of being issued."""
     import torch
     nb, hkv, bs, d = _pools(k_cache, v_cache)
     _need(block_tables, torch.int32, "block_tables")
@@ -225,21 +251,26 @@ def write_kv_at(k_cache, v_cache, k_new, v_new, block_tables, positions, seq_ids
     if t and (k_new.stride(2) != 1 or k_new.stride(1) != d or v_new.stride() != k_new.stride()):
         raise ValueError("k_new/v_new rows must be contiguous [Hkv][D] with one token stride")
     s, mb = block_tables.shape
-    _check("pa_write_kv_at", lib().pa_write_kv_at(
+    call = PreparedCall("pa_write_kv_at", (
         _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_tables), s, mb,
         _ptr(seq_ids), _ptr(positions), t, k_new.stride(0) if t else 0, nb, bs, hkv, d,
-        _dtype_code(k_cache), _ptr(slots_out), _stream(stream)))
+        _dtype_code(k_cache), _ptr(slots_out), _stream(stream)),
+        (k_cache, v_cache, k_new, v_new, block_tables, positions, seq_ids, slots_out), None)
+    return call if prepare else call()
 
 
-def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
-    """For each (src, dst) row of block_mapping [n][2]: block dst := block src."""
+def copy_blocks(k_cache, v_cache, block_mapping, stream=None, prepare=False):
+    """For each (src, dst) row of block_mapping [n][2]: block dst := block src.
+    With ``prepare=True`` the validated call is returned as a PreparedCall
+    instead of being issued."""
     import torch
     nb, hkv, bs, d = _pools(k_cache, v_cache)
     _need(block_mapping, torch.int32, "block_mapping")
     n = block_mapping.numel() // 2
-    _check("pa_copy_blocks", lib().pa_copy_blocks(
+    call = PreparedCall("pa_copy_blocks", (
         _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), n, nb, bs, hkv, d,
-        _dtype_code(k_cache), _stream(stream)))
+        _dtype_code(k_cache), _stream(stream)), (k_cache, v_cache, block_mapping), None)
+    return call if prepare else call()
 
 
 def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None):
@@ -297,31 +328,6 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
     return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                               block_size, max_context_len, partition_size, code,
                                               PA_DECODE_VECTOR_ONLY if vector_only else 0))
-
-
-class PreparedCall:
-    """One library call whose arguments were validated and marshalled once.
-
-    Calling it issues the same launch(es) again on the same stream, with the
-    same device buffers (their contents may change between calls): the
-    per-call host work is one foreign-function call.  The tensors the call
-    reads and writes are kept alive by the object.  ``result`` is what the
-    unprepared call returns (the output tensor)."""
-
-    __slots__ = ("_fn", "_name", "_args", "_keep", "result")
-
-    def __init__(self, name, args, keep, result):
-        self._fn = getattr(lib(), name)
-        self._name = name
-        self._args = tuple(args)
-        self._keep = keep
-        self.result = result
-
-    def __call__(self):
-        code = self._fn(*self._args)
-        if code != 0:
-            raise PAError(self._name, code)
-        return self.result
 
 
 def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,

@@ -172,6 +172,12 @@ class DeviceWorkload:
                     self.q, k, v, self.tables[table], self.ctx, wl.scale, self.max_ctx,
                     partition_size=part, workspace=self._ensure_workspace(part, False),
                     out=self.out, stream=stream, prepare=True, **kw))
+            elif kind == "write":
+                calls.append(pa.write_kv_at(k, v, x["k"], x["v"], self.tables[x["table"]],
+                                            x["positions"], seq_ids=x["seq_ids"],
+                                            slots_out=x["slots"], stream=stream, prepare=True))
+            elif kind == "copy":
+                calls.append(pa.copy_blocks(k, v, x, stream=stream, prepare=True))
             else:
                 calls.append(lambda op=op: self._run([op], pool, partition_size=part,
                                                      stream=stream, record_slots=False))
