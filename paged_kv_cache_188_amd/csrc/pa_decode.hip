@@ -94,6 +94,15 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
   return __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)));
 }
 
+// Streaming (non-temporal) stores of results that this kernel does not read
+// back: they leave no dirty L2 lines behind for the end-of-kernel write-back.
+__device__ __forceinline__ void store_stream(float* p, float4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_stream(uint16_t* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(p));
+}
+
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
@@ -373,8 +382,8 @@ __device__ __forceinline__ void mfma_finish(MfmaState<D>& st, int G, int lane, f
       float* dst = out_row0 + (int64_t)h * D + DV * col;
 #pragma unroll
       for (int c = 0; c < DV; c += 4)
-        *reinterpret_cast<float4*>(dst + c) = make_float4(
-            st.acc[c][r] * inv, st.acc[c + 1][r] * inv, st.acc[c + 2][r] * inv, st.acc[c + 3][r] * inv);
+        store_stream(dst + c, make_float4(st.acc[c][r] * inv, st.acc[c + 1][r] * inv,
+                                          st.acc[c + 2][r] * inv, st.acc[c + 3][r] * inv));
     } else {
       float* dst = acc_row0 + (int64_t)h * acc_stride + DV * col;
 #pragma unroll
@@ -671,12 +680,12 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
     const int w = c % 16;
     if (c < 16) {
       const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k_new) + row + 8 * w);
-      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.k_cache)) +
-                                cb + ((int64_t)w * bs + o) * 8) = x;
+      store_stream(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.k_cache)) + cb +
+                       ((int64_t)w * bs + o) * 8, x);
     } else {
       const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v_new) + row + 8 * w);
-      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.v_cache)) +
-                                cb + (int64_t)o * D + 8 * w) = x;
+      store_stream(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.v_cache)) + cb +
+                       (int64_t)o * D + 8 * w, x);
     }
     return;
   }
@@ -719,8 +728,8 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
       }
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    reinterpret_cast<float4*>(out + (int64_t)hd * D)[c] =
-        make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    store_stream(out + (int64_t)hd * D + 4 * c,
+                 make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv));
   }
 }
 
@@ -974,8 +983,7 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
       s.w += v.w;
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    reinterpret_cast<float4*>(p.out + row * D)[c] =
-        make_float4(s.x * inv, s.y * inv, s.z * inv, s.w * inv);
+    store_stream(p.out + row * D + 4 * c, make_float4(s.x * inv, s.y * inv, s.z * inv, s.w * inv));
   }
 }
 
