@@ -503,8 +503,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
       const float inv = base + tk >= 0 ? 1.0f / l_c : 0.f;
       float* dst = p.out + ((int64_t)(q0 + j0 + tk) * p.num_q_heads + (int64_t)kvh * G + hd) * D +
                    col;
+      // streaming stores: the output is not read back here, and the lines
+      // are not left dirty in L2 for the end-of-kernel write-back
 #pragma unroll
-      for (int nt = 0; nt < DV; ++nt) dst[16 * nt] = acc[h][nt][r] * inv;
+      for (int nt = 0; nt < DV; ++nt) __builtin_nontemporal_store(acc[h][nt][r] * inv, dst + 16 * nt);
     }
   }
 }
