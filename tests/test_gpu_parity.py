@@ -319,6 +319,38 @@ def test_prepared_call_equals_direct_call_bitwise(cid):
     assert res[0][1][1].tobytes() == res[1][1][1].tobytes()
 
 
+@pytest.mark.parametrize("cid", [2, 3])
+def test_append_with_bad_table_entry_writes_nothing_there(cid):
+    """A table entry outside the pool in the block that would receive a new
+    token: the append call skips that store (the pools equal the good call's
+    pools with that one slot left as it was), never writes block 0 in its
+    place, and every other sequence's output is unchanged bit for bit."""
+    wl = W.make(cid, small=True)
+    DeviceWorkload = _device()
+    good = DeviceWorkload(wl)
+    good.run_setup()
+    before_k, before_v = good.pool_bits()
+    out_good = good.run_step(append=True).cpu().numpy()
+    gk, gv = good.pool_bits()
+    bad = DeviceWorkload(wl)
+    bad.run_setup()
+    table = [x for kind, x in wl.step if kind == "decode"][0]
+    n0 = int(wl.context_lens[0])
+    blk = (n0 - 1) // wl.block_size
+    phys = int(wl.tables[table][0, blk])
+    bad.tables[table][0, blk] = wl.num_blocks + 5
+    out_bad = bad.run_step(append=True).cpu().numpy()
+    bk, bv = bad.pool_bits()
+    # the good call's pools with sequence 0's new slot as before the step
+    o = (n0 - 1) % wl.block_size
+    ek, ev = gk.copy(), gv.copy()
+    ek[phys, :, :, o, :] = before_k[phys, :, :, o, :]
+    ev[phys, :, o, :] = before_v[phys, :, o, :]
+    assert bk.tobytes() == ek.tobytes()
+    assert bv.tobytes() == ev.tobytes()
+    assert out_bad[1:].tobytes() == out_good[1:].tobytes()
+
+
 def test_workspace_reuse_with_new_queries():
     """Consecutive calls on one workspace: partials and arrival counters left
     by a call never leak into the next (new queries give the oracle's new
