@@ -617,13 +617,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
     phys = (phys >= 0 && phys < p.num_blocks) ? phys : 0;  // a bad entry reads block 0
     const int n = min(max(__builtin_amdgcn_readlane(dc.n_raw, l), 0), p.max_tokens);
     const int seg = seq * Hkv + kvh;
-    if (seg != cur_seg) {
-      if (cur_seg >= 0) finish_piece();
-      mfma_load_q<D>(p, seq, kvh * G, lane, qv);
-      st.reset();
-      cur_seg = seg;
-      cur_t0 = t;
-    }
+    const bool new_seg = seg != cur_seg;
+    // A new segment's Q and the tile are loaded before the finished piece is
+    // stored, so the waits on these loads need not cover those stores.
+    if (new_seg) mfma_load_q<D>(p, seq, kvh * G, lane, qv);
     const int64_t cb = ((int64_t)phys * Hkv + kvh) * ((int64_t)BS * D);
     const int valid = min(16, n - 16 * t);
     // The tile holding the sequence's new token (position n-1) when the call
@@ -644,6 +641,12 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
       load_tile2<D, BS>(kpool, vpool, cb, ((int64_t)phys2 * Hkv + kvh) * ((int64_t)BS * D), lane,
                         b, static_cast<const uint16_t*>(p.k_new) + row,
                         static_cast<const uint16_t*>(p.v_new) + row, append ? valid - 1 : -1);
+    }
+    if (new_seg) {
+      if (cur_seg >= 0) finish_piece();
+      st.reset();
+      cur_seg = seg;
+      cur_t0 = t;
     }
     compute_tile<D>(p, st, qv, b, valid, lane);
     cur_tlast = t;
