@@ -965,7 +965,27 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
   const int g = tid / C;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   const float4* acc = reinterpret_cast<const float4*>(p.ws_acc + row * P * D);
-  for (int i = g; i < np; i += PG) {
+  // eight partitions per round trip: their loads are issued before any is
+  // combined (the combination order is unchanged: partition by partition)
+  int i = g;
+  for (; i + 7 * PG < np; i += 8 * PG) {
+    float mv[8];
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      mv[u] = m[i + u * PG];
+      v[u] = acc[(int64_t)(i + u * PG) * C + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = fast_exp2(mv[u] - M);
+      a.x = fmaf(w, v[u].x, a.x);
+      a.y = fmaf(w, v[u].y, a.y);
+      a.z = fmaf(w, v[u].z, a.z);
+      a.w = fmaf(w, v[u].w, a.w);
+    }
+  }
+  for (; i < np; i += PG) {
     const float w = fast_exp2(m[i] - M);
     const float4 v = acc[(int64_t)i * C + c];
     a.x = fmaf(w, v.x, a.x);
