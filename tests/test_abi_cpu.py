@@ -289,3 +289,11 @@ def test_probe_validation(lib):
 def test_probe_gather_batch_limit(lib):
     assert lib.pa_probe_gather(FAKE, FAKE, FAKE, 4, FAKE, 16385, 2, 128, 16, 10, 1, FAKE, 64,
                                NULL) == UNSUP
+
+
+def test_one_hip_runtime_in_the_process(lib):
+    """libpa binds to the HIP runtime torch already loaded (same soname), so
+    torch's streams and device pointers are valid inside the library: after
+    loading it, exactly one libamdhip64 file is mapped in this process."""
+    mapped = {line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line}
+    assert len(mapped) == 1, mapped
