@@ -59,6 +59,15 @@ __global__ __launch_bounds__(256) void compute_slots_kernel(
                         block_size, num_blocks);
 }
 
+// Workgroups are dealt to the 8 XCDs of the chip in turn (workgroup b to XCD
+// b mod 8).  Renumbered so that each XCD takes one contiguous run of tokens:
+// the K granules of consecutive tokens of a block share cache lines, which
+// one L2 then merges whole before writing them back.
+__device__ __forceinline__ int xcd_run(int b, int n) {
+  const int x = b % 8, k = b / 8, q = n / 8, r = n % 8;
+  return x * q + min(x, r) + k;
+}
+
 // One wave per token; each lane moves 16-byte granules of the token's
 // [Hkv][D] row to their places in the two pools.
 constexpr int kWriteWaves = 4;
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_kernel(
     int64_t pool_slots, int block_size, int num_kv_heads, int head_chunks) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int j = blockIdx.x * kWriteWaves + wave;
+  const int j = xcd_run(blockIdx.x, gridDim.x) * kWriteWaves + wave;
   if (j >= num_tokens) return;
   const int64_t slot = slot_mapping[j];
   if (slot < 0 || slot >= pool_slots) return;  // padding token, or outside the pool
@@ -117,7 +126,7 @@ __global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_at_kernel(
     int block_size, int num_kv_heads, int head_chunks) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int j = blockIdx.x * kWriteWaves + wave;
+  const int j = xcd_run(blockIdx.x, gridDim.x) * kWriteWaves + wave;
   if (j >= num_tokens) return;
   const int64_t slot = token_slot(block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions,
                                   j, block_size, num_blocks);
