@@ -426,6 +426,27 @@ def other_ops_timing(torch, dev, wl, npools, stream, reps=20):
     return res
 
 
+def history_write_timing(torch, dev, wl, stream, reps=5):
+    """The workload's history fill at scale: each setup write
+    (pa_write_kv_at of every cached token) timed alone, one event pair around
+    reps back-to-back calls; bytes are the K/V rows read plus written."""
+    e = 2 if wl.dtype == "bf16" else 4
+    out = []
+    for op in dev.setup_ops:
+        kind, x = op
+        if kind != "write":
+            continue
+        call = dev.prepare([op], 0, stream=stream)[0]
+        call()
+        ms = _span_ms(torch, stream, lambda r: call(), reps)
+        t = int(x["positions"].numel())
+        nbytes = 2 * 2 * t * wl.num_kv_heads * wl.head_dim * e + 20 * t
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out.append({"call": "pa_write_kv_at", "tokens": t, "us": round(ms * 1e3, 1),
+                    "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+    return out
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -457,6 +478,7 @@ def main():
         wl.partition_size = args.partition
     dev = DeviceWorkload(wl)
     dev.run_setup()
+    hist = history_write_timing(torch, dev, wl, torch.cuda.current_stream())
     dev.release_setup_inputs()
     pool_bytes = 2 * dev.pools[0][0].numel() * dev.pools[0][0].element_size()
     npools = max(2, min(8, -(-4 * LLC_BYTES // pool_bytes) + 1))
@@ -596,6 +618,7 @@ def main():
         },
     }
     res["other_ops"] = ops_timing
+    res["history_write"] = hist
     uniq = wl.unique_kv_bytes()
     if uniq < kv_bytes:
         # blocks shared between sequences: the call reads each sequence's

@@ -136,6 +136,145 @@ __global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_at_kernel(
               num_kv_heads, head_chunks, lane);
 }
 
+// Tokens are taken 16 at a time, one workgroup of four waves per group
+// (workgroups renumbered with xcd_run).  The K rows of the group are staged
+// in LDS, so that the loads read whole token rows and the stores write, for
+// each (head, granule), the 16 tokens' granules with 16 consecutive threads:
+// when the tokens sit at consecutive offsets of a block (a prompt chunk or a
+// history written in order) those granules are one contiguous 256-byte run
+// of the K pool.  V rows go straight through (a token's row is contiguous in
+// the V pool).  Every token is stored at its own slot, so any slot pattern
+// is handled; tokens with no slot (padding, outside the table or the pool)
+// are skipped.  Rows wider than the LDS staging (more than kRunMaxChunks
+// granules) take a per-token path, each wave four tokens with all their
+// loads issued before their stores.
+constexpr int kRunTokens = 16;
+constexpr int kRunThreads = kWriteWaves * kWave;
+// LDS staging: 16 tokens x (nchunks + 1) granules, kept under 64 KiB
+constexpr int kRunMaxChunks = 240;
+// Fewer tokens than this (a decode step's one token per sequence) go one
+// wave per token instead: the latency of a small write is lower that way
+// (64 tokens: ~4 us against ~6 us staged), and there are no runs to gain.
+constexpr int kRunMinTokens = 1024;
+
+__global__ __launch_bounds__(kRunThreads) void write_kv_runs_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ block_tables,
+    int num_seqs, int max_blocks_per_seq, const int32_t* __restrict__ seq_ids,
+    const int32_t* __restrict__ positions, int64_t* __restrict__ slots_out, int num_tokens,
+    int64_t token_stride_bytes, int num_blocks, int block_size, int num_kv_heads,
+    int head_chunks) {
+  extern __shared__ uint4 s_k[];  // [16][nchunks + 1] granules
+  // byte offsets of granule 0 of each token's K and V rows in the pools, or -1
+  __shared__ int64_t s_kbase[kRunTokens], s_vbase[kRunTokens];
+  const int tid = threadIdx.x;
+  const int j0 = xcd_run(blockIdx.x, gridDim.x) * kRunTokens;
+  const int64_t pool_slots = (int64_t)num_blocks * block_size;
+  if (tid < kRunTokens) {
+    const int j = j0 + tid;
+    int64_t slot = -1;
+    if (j < num_tokens) {
+      if (slot_mapping) {
+        slot = slot_mapping[j];
+        if (slot >= pool_slots) slot = -1;  // outside the pool: skipped
+      } else {
+        slot = token_slot(block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions, j,
+                          block_size, num_blocks);
+        if (slots_out) slots_out[j] = slot;
+      }
+    }
+    int64_t kb = -1, vb = -1;
+    if (slot >= 0) {
+      const int64_t blk = slot / block_size, off = slot - blk * block_size;
+      // K element (h, granule w) at ((blk*Hkv + h)*hc + w)*bs + off; V at
+      // ((blk*Hkv + h)*bs + off)*hc + w (granules of 16 bytes)
+      kb = (blk * num_kv_heads * head_chunks * block_size + off) * 16;
+      vb = (blk * num_kv_heads * block_size + off) * head_chunks * 16;
+    }
+    s_kbase[tid] = kb;
+    s_vbase[tid] = vb;
+  }
+  __syncthreads();
+  const int nchunks = num_kv_heads * head_chunks;  // granules per token row
+  const int64_t vhead = (int64_t)block_size * head_chunks * 16;  // V bytes per (block, head)
+  const int64_t kgran = (int64_t)block_size * 16;                // K bytes per (block, head, granule)
+  if (nchunks <= kRunMaxChunks) {
+    const int row = nchunks + 1;  // padded LDS row: the transposed reads hit distinct banks
+    const int total = kRunTokens * nchunks;
+    // eight granules of K and of V per thread in flight: all loads of a batch
+    // are issued before any of them is stored
+    constexpr int kBatch = 8;
+    for (int e0 = tid; e0 < total; e0 += kBatch * kRunThreads) {
+      uint4 kx[kBatch], vx[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = e0 + u * kRunThreads;
+        const int i = e / nchunks, c = e - i * nchunks;
+        kx[u] = vx[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (e < total && s_vbase[i] >= 0) {
+          const int64_t src = (int64_t)(j0 + i) * token_stride_bytes + (int64_t)c * 16;
+          kx[u] = *reinterpret_cast<const uint4*>(k_new + src);
+          vx[u] = *reinterpret_cast<const uint4*>(v_new + src);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = e0 + u * kRunThreads;
+        const int i = e / nchunks, c = e - i * nchunks;
+        if (e < total && s_vbase[i] >= 0) {
+          s_k[i * row + c] = kx[u];
+          const int h = c / head_chunks, w = c - h * head_chunks;
+          store_stream(v_cache + s_vbase[i] + h * vhead + w * 16, vx[u]);
+        }
+      }
+    }
+    __syncthreads();
+    // Whole runs (the 16 tokens at offsets 16m .. 16m+15 of one block) are
+    // streamed; partial runs use ordinary stores, so that L2 merges them with
+    // the neighbouring group's part of the same lines (written by the same
+    // XCD, see xcd_run) before write-back.
+    bool whole = s_kbase[0] >= 0 && block_size % kRunTokens == 0 &&
+                 (s_kbase[0] / 16) % kRunTokens == 0;
+#pragma unroll
+    for (int i = 1; i < kRunTokens; ++i) whole = whole && s_kbase[i] == s_kbase[0] + 16 * i;
+    for (int e = tid; e < kRunTokens * nchunks; e += kRunThreads) {
+      const int c = e / kRunTokens, i = e - c * kRunTokens;  // (head, granule) c, token i
+      const int64_t kb = s_kbase[i];
+      if (kb < 0) continue;
+      if (whole)
+        store_stream(k_cache + kb + c * kgran, s_k[i * row + c]);
+      else
+        *reinterpret_cast<uint4*>(k_cache + kb + c * kgran) = s_k[i * row + c];
+    }
+    return;
+  }
+  // per-token path: wave v takes tokens j0 + 4v .. j0 + 4v + 3
+  const int wave = tid / kWave, lane = tid % kWave;
+  for (int c = lane; c < nchunks; c += kWave) {
+    const int h = c / head_chunks, w = c - h * head_chunks;
+    uint4 a[4], b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      a[t] = b[t] = make_uint4(0u, 0u, 0u, 0u);
+      if (s_vbase[4 * wave + t] < 0) continue;
+      const int64_t src = (int64_t)(j0 + 4 * wave + t) * token_stride_bytes + (int64_t)c * 16;
+      a[t] = *reinterpret_cast<const uint4*>(k_new + src);
+      b[t] = *reinterpret_cast<const uint4*>(v_new + src);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t kb = s_kbase[4 * wave + t], vb = s_vbase[4 * wave + t];
+      if (vb < 0) continue;
+      // K granules of consecutive tokens of a block share lines, which
+      // ordinary stores let L2 merge before write-back; a V row is whole
+      // lines, streamed
+      *reinterpret_cast<uint4*>(k_cache + kb + c * kgran) = a[t];
+      store_stream(v_cache + vb + h * vhead + w * 16, b[t]);
+    }
+  }
+}
+
 // grid = (pair, pool K/V, 16 KiB piece of the block).  Each thread moves up
 // to four 16-byte chunks, all loads issued before the stores.  The loads are
 // ordinary (the 8 copies of one shared block read the same source), the
@@ -193,12 +332,24 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
                            int num_blocks, int block_size, int num_kv_heads, int head_bytes,
                            hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const int grid = (num_tokens + kWriteWaves - 1) / kWriteWaves;
-  hipLaunchKernelGGL(write_kv_kernel, dim3(grid), dim3(kWriteWaves * kWave), 0, stream,
-                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
-                     static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
-                     slot_mapping, num_tokens, token_stride_bytes,
-                     (int64_t)num_blocks * block_size, block_size, num_kv_heads, head_bytes / 16);
+  if (num_tokens < kRunMinTokens) {
+    const int grid = (num_tokens + kWriteWaves - 1) / kWriteWaves;
+    hipLaunchKernelGGL(write_kv_kernel, dim3(grid), dim3(kWriteWaves * kWave), 0, stream,
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                       static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
+                       slot_mapping, num_tokens, token_stride_bytes,
+                       (int64_t)num_blocks * block_size, block_size, num_kv_heads,
+                       head_bytes / 16);
+    return hipGetLastError();
+  }
+  const int nchunks = num_kv_heads * (head_bytes / 16);
+  const size_t lds = nchunks <= kRunMaxChunks ? (size_t)kRunTokens * (nchunks + 1) * 16 : 0;
+  hipLaunchKernelGGL(write_kv_runs_kernel, dim3((num_tokens + kRunTokens - 1) / kRunTokens),
+                     dim3(kRunThreads), lds, stream, static_cast<uint8_t*>(k_cache),
+                     static_cast<uint8_t*>(v_cache), static_cast<const uint8_t*>(k_new),
+                     static_cast<const uint8_t*>(v_new), slot_mapping, nullptr, 0, 0, nullptr,
+                     nullptr, nullptr, num_tokens, token_stride_bytes, num_blocks, block_size,
+                     num_kv_heads, head_bytes / 16);
   return hipGetLastError();
 }
 
@@ -246,13 +397,24 @@ hipError_t launch_write_kv_at(void* k_cache, void* v_cache, const void* k_new, c
                               int num_blocks, int block_size, int num_kv_heads, int head_bytes,
                               hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  const int grid = (num_tokens + kWriteWaves - 1) / kWriteWaves;
-  hipLaunchKernelGGL(write_kv_at_kernel, dim3(grid), dim3(kWriteWaves * kWave), 0, stream,
-                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
-                     static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
-                     block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions, slots_out,
-                     num_tokens, token_stride_bytes, num_blocks, block_size, num_kv_heads,
-                     head_bytes / 16);
+  if (num_tokens < kRunMinTokens) {
+    const int grid = (num_tokens + kWriteWaves - 1) / kWriteWaves;
+    hipLaunchKernelGGL(write_kv_at_kernel, dim3(grid), dim3(kWriteWaves * kWave), 0, stream,
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                       static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
+                       block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions, slots_out,
+                       num_tokens, token_stride_bytes, num_blocks, block_size, num_kv_heads,
+                       head_bytes / 16);
+    return hipGetLastError();
+  }
+  const int nchunks = num_kv_heads * (head_bytes / 16);
+  const size_t lds = nchunks <= kRunMaxChunks ? (size_t)kRunTokens * (nchunks + 1) * 16 : 0;
+  hipLaunchKernelGGL(write_kv_runs_kernel, dim3((num_tokens + kRunTokens - 1) / kRunTokens),
+                     dim3(kRunThreads), lds, stream, static_cast<uint8_t*>(k_cache),
+                     static_cast<uint8_t*>(v_cache), static_cast<const uint8_t*>(k_new),
+                     static_cast<const uint8_t*>(v_new), nullptr, block_tables, num_seqs,
+                     max_blocks_per_seq, seq_ids, positions, slots_out, num_tokens,
+                     token_stride_bytes, num_blocks, block_size, num_kv_heads, head_bytes / 16);
   return hipGetLastError();
 }
 
