@@ -331,8 +331,9 @@ def measured_traffic(wl):
 
 
 def calibrate_copy(steps):
-    """Copy 8192 blocks of 32 KiB in each of the K and V pools: 256 MiB read
-    and 256 MiB written per launch, with no reuse between launches."""
+    """Copy 8192 blocks of 32 KiB in each of the K and V pools: 512 MiB read
+    and 512 MiB written per launch (536,870,912 B each way), with no reuse
+    between launches."""
     import torch
 
     import paged_kv_cache_188_amd as pa

@@ -50,6 +50,12 @@
  *                      so the matrix-core operand of 16 keys x 16 bytes is one
  *                      contiguous run).  In both pools one (block, KV head)
  *                      chunk is block_size*head_dim contiguous elements.
+ *                      K is deliberately not token-major like V
+ *                      ([NB][Hkv][bs][D]): with token-major rows the four
+ *                      lanes of each 64-byte group of the matrix-core K
+ *                      operand would read four different 256-byte rows, and
+ *                      a gather of that pattern measured ~4.7 TB/s on MI355X
+ *                      against ~6.0 TB/s for the granule layout.
  *   block_tables       int32 [num_seqs][max_blocks_per_seq]; entry b is the
  *                      physical block of logical block b; entries past the
  *                      last used block are never read (may hold -1)
@@ -68,8 +74,11 @@
  *   access that would leave its buffer, so a bad table cannot make the GPU
  *   fault; the affected results are then unspecified.  A launch failure is
  *   reported as PA_ERR_HIP.
- * Threading.  No mutable global state; concurrent calls on different streams
- *   are safe when their output buffers are disjoint.
+ * Threading.  The only state the library keeps is a per-device cache of the
+ *   stream-K worker count (resident wave slots of the device, read once per
+ *   device and head_dim; written atomically), so concurrent calls on
+ *   different streams are safe when their output and workspace buffers are
+ *   disjoint.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -83,7 +92,17 @@ extern "C" {
 
 #define PA_ABI_VERSION 1
 
-typedef enum pa_status {
+/* In C++ the enums get int as their fixed underlying type, so every int a C
+ * caller passes is a value of the type (a plain C++ enum would make an
+ * out-of-range value undefined behaviour before validation could reject
+ * it); in C an enum is an int-sized integer anyway, so the ABI is the same. */
+#ifdef __cplusplus
+#define PA_ENUM_BASE : int
+#else
+#define PA_ENUM_BASE
+#endif
+
+typedef enum pa_status PA_ENUM_BASE {
   PA_OK = 0,
   PA_ERR_NULL = 1,         /* a required pointer is NULL                     */
   PA_ERR_SHAPE = 2,        /* a size is out of range or sizes disagree       */
@@ -94,7 +113,7 @@ typedef enum pa_status {
   PA_ERR_CAPACITY = 7      /* block manager: no free block / sequence slot   */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum pa_dtype PA_ENUM_BASE { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
 /* Supported shapes (checked by every entry point):
  *   head_dim   in {64, 128}
@@ -224,13 +243,17 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k,
  *     s_t   = scale * dot(q[i][h], K_t[g])           t = 0..n-1
  *     out[i][h] = sum_t softmax(s)_t * V_t[g]        (float32 result)
  * where K_t / V_t is token t's row reached through block_tables[i].
- * n == 0 gives zeros.  n is clamped to [0, max_blocks_per_seq*block_size].
+ * n == 0 gives zeros.  n is clamped as described under max_context_len.
  * Scores, softmax and the weighted sum are accumulated in float32 from the
  * exact float32 values of the stored elements.
  *
  * max_context_len is a host-side upper bound of every context_lens[i]; it
  * sizes the fixed-partition grid and workspace (a larger bound is correct,
- * just slower).
+ * just slower).  On every path a context is clamped to
+ *     min(context_lens[i], max_context_len, max_blocks_per_seq*block_size)
+ * tokens, so a bound below some context_lens[i] truncates that context to
+ * its first max_context_len tokens (and, for the append call, the new token
+ * at position context_lens[i]-1 is then neither stored nor attended).
  *
  * Work decomposition.  With partition_size == 0, bf16 K/V, flags == 0 and
  * num_seqs <= 8192 the library splits the (sequence, KV head, 16-token tile)
@@ -248,7 +271,11 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k,
  * (fixed partitions) instead of the matrix-core kernel; both give results
  * within the same tolerance, the flag exists for cross-checking.
  * The result is deterministic: it depends on the logical contents and the
- * partitioning only, never on physical block ids or on timing.
+ * decomposition only, never on physical block ids or on timing.  The
+ * fixed-partition decomposition is fixed by the arguments; the stream-K one
+ * also by the device (its compute-unit count and the kernel's occupancy, see
+ * pa_decode_streamk_workers), so two devices of different sizes may round
+ * differently, within the same tolerance.
  * ------------------------------------------------------------------------- */
 #define PA_DECODE_VECTOR_ONLY 1u
 
@@ -314,7 +341,6 @@ pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache,
                                      size_t workspace_bytes, pa_dtype dtype,
                                      uint32_t flags, void* stream);
 
-/* Text of a status code (static storage). */
 /* ---------------------------------------------------------------------------
  * pa_prefill_attention  (multi-query paged attention: a prompt chunk)
  *
@@ -349,7 +375,9 @@ pa_status pa_prefill_attention(float* out, const void* q, const void* k_cache,
                                int32_t max_query_len, float scale,
                                pa_dtype dtype, void* stream);
 
-const char* pa_status_string(pa_status status);
+/* Text of a status code (static storage).  Takes any integer (a pa_status
+ * value or not); codes that are not a pa_status give "unknown status". */
+const char* pa_status_string(int status);
 
 /* PA_ABI_VERSION of the built library. */
 int32_t pa_abi_version(void);

@@ -18,7 +18,7 @@
  *   [nalar]    "PagedAttention: memetakan blok KV logis ke memori fisik tidak
  *              kontigu", "Urutan logis dipisahkan dari penempatan fisik"
  *              (a new physical block when a sequence crosses a block
- *              boundary), "Sisa alokasi tetap ada, tetapi dibatasi ukuran
+ *              boundary), "Sisa alokasi dibatasi oleh granularitas
  *              blok" (waste bounded by the block size), "Sharing blok dapat
  *              menghindari duplikasi state KV" (shared while unchanged; a
  *              writer gets its own copy).

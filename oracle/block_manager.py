@@ -13,8 +13,8 @@ What it models, from the pages (cited by title and section):
   copied block (copy-on-write).
 * [nalar] "PagedAttention: memetakan blok KV logis ke memori fisik tidak
   kontigu": "Urutan logis dipisahkan dari penempatan fisik" (a new physical
-  block when a sequence crosses a block boundary); "Sisa alokasi tetap ada,
-  tetapi dibatasi ukuran blok" (only the last block of a sequence can be
+  block when a sequence crosses a block boundary); "Sisa alokasi dibatasi
+  oleh granularitas blok" (only the last block of a sequence can be
   partly empty); "Sharing blok dapat menghindari duplikasi state KV" (a block
   is shared while its content is unchanged; a writer gets separate storage).
 * [bicarait] "Melihat Lebih Dalam vLLM v0.7 ...", "Blueprint Arsitektur 2"

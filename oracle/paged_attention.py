@@ -158,7 +158,8 @@ def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
     """Return copies of the pools with each new token's K/V stored in its slot.
 
     [gyaansetu] "Apa itu KV Cache?": K and V are computed for the new token only
-    and kept for later steps.  Pools are ``[NB][Hkv][bs][D]``; ``k_new`` and
+    and kept for later steps.  Pools are K ``[NB][Hkv][D/x][bs][x]`` and V
+    ``[NB][Hkv][bs][D]``; ``k_new`` and
     ``v_new`` are ``[T][Hkv][D]``.  The copy is of bits, so it is exact for any
     element type.  Slot -1 skips the token; a slot outside the pool or two
     tokens with the same slot raise.  K rows are stored as granules (see the

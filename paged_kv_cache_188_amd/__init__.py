@@ -18,7 +18,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# PA_LIBRARY may name another build of the same library (the host-sanitized
+# one of build.py --sanitize); by default the in-tree libpa.so is loaded.
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32 = 0
 PA_BF16 = 1
@@ -154,6 +157,13 @@ def _pools(k_cache, v_cache):
     return nb, hkv, bs, dx * x
 
 
+def _shape(t, shape, name):
+    """ValueError unless tensor t (if given) has exactly `shape`: a buffer of
+    the wrong size would make a kernel read or write past its end."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _need(t, dtype, name):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -197,11 +207,15 @@ def compute_slots(block_tables, positions, block_size, num_blocks, seq_ids=None,
     """slot[j] = table[seq][pos // bs] * bs + pos % bs (int64), -1 for padding
     or invalid tokens.  ``seq_ids=None``: token j belongs to sequence j."""
     import torch
+    if block_tables.dim() != 2 or positions.dim() != 1:
+        raise ValueError("block_tables must be [S][MB] and positions [T]")
+    n = positions.numel()
+    _shape(seq_ids, (n,), "seq_ids")
+    _shape(out, (n,), "out")
     _need(block_tables, torch.int32, "block_tables")
     _need(positions, torch.int32, "positions")
     if seq_ids is not None:
         _need(seq_ids, torch.int32, "seq_ids")
-    n = positions.numel()
     if out is None:
         out = torch.empty(n, dtype=torch.int64, device=positions.device)
     _need(out, torch.int64, "out")
@@ -236,6 +250,10 @@ def write_kv_at(k_cache, v_cache, k_new, v_new, block_tables, positions, seq_ids
     ``slots_out`` when given.  With ``prepare=True`` the validated call is
     returned as a PreparedCall instead of being issued."""
     import torch
+    if block_tables.dim() != 2 or positions.dim() != 1:
+        raise ValueError("block_tables must be [S][MB] and positions [T]")
+    _shape(seq_ids, positions.shape, "seq_ids")
+    _shape(slots_out, positions.shape, "slots_out")
     nb, hkv, bs, d = _pools(k_cache, v_cache)
     _need(block_tables, torch.int32, "block_tables")
     _need(positions, torch.int32, "positions")
@@ -264,9 +282,11 @@ def copy_blocks(k_cache, v_cache, block_mapping, stream=None, prepare=False):
     With ``prepare=True`` the validated call is returned as a PreparedCall
     instead of being issued."""
     import torch
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [n][2] (src, dst)")
     nb, hkv, bs, d = _pools(k_cache, v_cache)
     _need(block_mapping, torch.int32, "block_mapping")
-    n = block_mapping.numel() // 2
+    n = block_mapping.shape[0]
     call = PreparedCall("pa_copy_blocks", (
         _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), n, nb, bs, hkv, d,
         _dtype_code(k_cache), _stream(stream)), (k_cache, v_cache, block_mapping), None)
@@ -278,12 +298,14 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None):
     tensor): block dst of (dst_k, dst_v) := block src of (src_k, src_v).
     Either pool pair may be pinned host tensors (pin_memory=True)."""
     import torch
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [n][2] (src, dst)")
     dnb, hkv, bs, d = _host_or_device_pools(dst_k, dst_v)
     snb, hkv2, bs2, d2 = _host_or_device_pools(src_k, src_v)
     if (hkv, bs, d) != (hkv2, bs2, d2) or dst_k.dtype != src_k.dtype:
         raise ValueError("the two pool pairs disagree in block shape or element type")
     _need(block_mapping, torch.int32, "block_mapping")
-    n = block_mapping.numel() // 2
+    n = block_mapping.shape[0]
     _check("pa_swap_blocks", lib().pa_swap_blocks(
         _ptr(dst_k), _ptr(dst_v), _ptr(src_k), _ptr(src_v), _ptr(block_mapping), n, snb, dnb,
         bs, hkv, d, _dtype_code(src_k), _stream(stream)))
@@ -341,14 +363,19 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max
     the validated call is returned as a PreparedCall, to be issued later (as
     often as wanted) with the same buffers."""
     import torch
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [S][Hq][D] and block_tables [S][MB]")
     s, hq, d = q.shape
+    mb = block_tables.shape[1]
+    _shape(block_tables, (s, mb), "block_tables")
+    _shape(context_lens, (s,), "context_lens")
+    _shape(out, (s, hq, d), "out")
     nb, hkv, bs, d2 = _pools(k_cache, v_cache)
     if d2 != d:
         raise ValueError("q and the pools disagree in head_dim")
     _need(q, k_cache.dtype, "q")
     _need(block_tables, torch.int32, "block_tables")
     _need(context_lens, torch.int32, "context_lens")
-    mb = block_tables.shape[1]
     need = decode_workspace_size(s, hq, hkv, d, bs, max_context_len, partition_size,
                                  k_cache.dtype, vector_only)
     if workspace is None and need:
@@ -387,7 +414,13 @@ def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_sta
     query_start[i+1]-1 (int32 [S+1]); its chunk ends its context
     context_lens[i] and attends causally (pa_prefill_attention)."""
     import torch
+    if q.dim() != 3 or context_lens.dim() != 1 or block_tables.dim() != 2:
+        raise ValueError("q must be [T][Hq][D], context_lens [S] and block_tables [S][MB]")
     t, hq, d = q.shape
+    s = context_lens.shape[0]
+    if query_start.shape != (s + 1,) or block_tables.shape[0] != s:
+        raise ValueError("query_start must be [S+1] and block_tables [S][MB]")
+    _shape(out, (t, hq, d), "out")
     nb, hkv, bs, d2 = _pools(k_cache, v_cache)
     if d2 != d:
         raise ValueError("q and the pools disagree in head_dim")
@@ -395,9 +428,6 @@ def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_sta
     _need(block_tables, torch.int32, "block_tables")
     _need(context_lens, torch.int32, "context_lens")
     _need(query_start, torch.int32, "query_start")
-    s = context_lens.shape[0]
-    if query_start.shape != (s + 1,) or block_tables.shape[0] != s:
-        raise ValueError("query_start must be [S+1] and block_tables [S][MB]")
     if out is None:
         out = torch.empty((t, hq, d), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")

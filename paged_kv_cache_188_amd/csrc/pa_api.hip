@@ -80,7 +80,8 @@ extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 
-const char* pa_status_string(pa_status s) {
+const char* pa_status_string(int s) {
+  // an int, not a pa_status: an out-of-range enum value would be undefined
   switch (s) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
@@ -290,7 +291,10 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
   if (flags & ~PA_DECODE_VECTOR_ONLY) return PA_ERR_UNSUPPORTED;
   if (partition_size != 0 && !valid_partition(partition_size, block_size)) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_SHAPE;
-  const int32_t max_tokens = max_blocks_per_seq * block_size;
+  // every context is clamped to the caller's bound and to what the table holds
+  const int32_t max_tokens = max_context_len < max_blocks_per_seq * block_size
+                                 ? max_context_len
+                                 : max_blocks_per_seq * block_size;
   const bool vector_only = (flags & PA_DECODE_VECTOR_ONLY) != 0;
   const pa::DecodePath path =
       pa::decode_path(num_seqs, block_size, dtype, partition_size, vector_only);
@@ -363,12 +367,12 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
   } else {
     p.partition = part;
     p.max_partitions = (int)P;
-    p.max_tokens = (int)((int64_t)P * part < max_tokens ? (int64_t)P * part : max_tokens);
+    p.max_tokens = max_tokens;  // <= P * part, so every token lies in a partition
     if (append) {  // store the new tokens first, then attend
       const pa_status st = from_hip(pa::launch_append_kv(
           const_cast<void*>(k_cache), const_cast<void*>(v_cache), k_new, v_new,
           new_token_stride * e, block_tables, context_lens, num_seqs, max_blocks_per_seq,
-          num_blocks, block_size, num_kv_heads, head_dim * e, hs));
+          max_tokens, num_blocks, block_size, num_kv_heads, head_dim * e, hs));
       if (st != PA_OK) return st;
     }
   }

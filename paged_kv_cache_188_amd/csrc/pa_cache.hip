@@ -359,13 +359,13 @@ __global__ __launch_bounds__(kWriteWaves * kWave) void append_kv_kernel(
     const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
     int64_t token_stride_bytes, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int num_seqs, int max_blocks_per_seq,
-    int num_blocks, int block_size, int num_kv_heads, int head_chunks) {
+    int max_tokens, int num_blocks, int block_size, int num_kv_heads, int head_chunks) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int i = blockIdx.x * kWriteWaves + wave;
   if (i >= num_seqs) return;
   const int n = context_lens[i];
-  if (n < 1 || (int64_t)n > (int64_t)max_blocks_per_seq * block_size) return;
+  if (n < 1 || n > max_tokens) return;  // max_tokens <= max_blocks_per_seq * block_size
   const int pos = n - 1;
   const int b = pos / block_size;
   const int phys = block_tables[(int64_t)i * max_blocks_per_seq + b];
@@ -378,15 +378,16 @@ __global__ __launch_bounds__(kWriteWaves * kWave) void append_kv_kernel(
 hipError_t launch_append_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             int64_t token_stride_bytes, const int32_t* block_tables,
                             const int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
-                            int num_blocks, int block_size, int num_kv_heads, int head_bytes,
-                            hipStream_t stream) {
+                            int max_tokens, int num_blocks, int block_size, int num_kv_heads,
+                            int head_bytes, hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
   const int grid = (num_seqs + kWriteWaves - 1) / kWriteWaves;
   hipLaunchKernelGGL(append_kv_kernel, dim3(grid), dim3(kWriteWaves * kWave), 0, stream,
                      static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
                      static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
                      token_stride_bytes, block_tables, context_lens, num_seqs,
-                     max_blocks_per_seq, num_blocks, block_size, num_kv_heads, head_bytes / 16);
+                     max_blocks_per_seq, max_tokens, num_blocks, block_size, num_kv_heads,
+                     head_bytes / 16);
   return hipGetLastError();
 }
 

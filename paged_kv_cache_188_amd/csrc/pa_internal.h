@@ -30,13 +30,13 @@ hipError_t launch_write_kv_at(void* k_cache, void* v_cache, const void* k_new, c
                               hipStream_t stream);
 
 // Store row i of k_new / v_new at position context_lens[i]-1 of sequence i
-// (skipped for an empty context, a context beyond max_blocks*block_size, or
-// an invalid table entry).  One wave per sequence.
+// (skipped for an empty context, a context beyond max_tokens <=
+// max_blocks*block_size, or an invalid table entry).  One wave per sequence.
 hipError_t launch_append_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             int64_t token_stride_bytes, const int32_t* block_tables,
                             const int32_t* context_lens, int num_seqs, int max_blocks_per_seq,
-                            int num_blocks, int block_size, int num_kv_heads, int head_bytes,
-                            hipStream_t stream);
+                            int max_tokens, int num_blocks, int block_size, int num_kv_heads,
+                            int head_bytes, hipStream_t stream);
 
 // Block block_mapping[n][0] of the source pools -> block block_mapping[n][1]
 // of the destination pools (pairs outside either pool are skipped).
@@ -74,7 +74,8 @@ struct DecodeParams {
   int block_size;
   int partition;      // fixed-partition path: tokens per partition
   int max_partitions; // fixed-partition path: P = ceil(max_context_len / partition)
-  int max_tokens;     // every context length is clamped to it, so no index leaves its buffer
+  int max_tokens;     // every context length is clamped to it (min of the caller's bound and
+                      // max_blocks_per_seq * block_size), so no index leaves its buffer
   int max_workers;    // stream-K path: waves launched (slot capacity of the workspace)
   float scale_log2;   // scale * log2(e)
 };

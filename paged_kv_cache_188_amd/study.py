@@ -1,6 +1,6 @@
 """Paging overhead and block size, measured with the decode kernels.
 
-[nalar] "Sisa alokasi tetap ada, tetapi dibatasi ukuran blok" trades tail
+[nalar] "Sisa alokasi dibatasi oleh granularitas blok" trades tail
 waste (the unused slots of each sequence's last block) against metadata
 (table entries) as the block size changes, and [nalar] "Kernel attention
 harus mengikuti block table" notes that walking the table costs something.

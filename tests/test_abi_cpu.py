@@ -297,3 +297,42 @@ def test_one_hip_runtime_in_the_process(lib):
     loading it, exactly one libamdhip64 file is mapped in this process."""
     mapped = {line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line}
     assert len(mapped) == 1, mapped
+
+
+def test_binding_checks_buffer_shapes_before_any_call():
+    """The Python wrappers refuse tensors whose shapes disagree with the
+    sizes passed to the kernels (a short table, length array or output would
+    be read or written past its end).  The checks come before any device
+    check, so CPU tensors show them here."""
+    import torch
+    bf = torch.bfloat16
+    S, Hq, Hkv, D, bs, NB, MB = 4, 8, 2, 64, 16, 32, 3
+    k = torch.zeros((NB, Hkv, D // 8, bs, 8), dtype=bf)
+    v = torch.zeros((NB, Hkv, bs, D), dtype=bf)
+    q = torch.zeros((S, Hq, D), dtype=bf)
+    bt = torch.zeros((S, MB), dtype=torch.int32)
+    ctx = torch.ones(S, dtype=torch.int32)
+    with pytest.raises(ValueError, match="block_tables"):
+        pa.decode_attention(q, k, v, bt[:S - 1], ctx, 0.125, 16)
+    with pytest.raises(ValueError, match="context_lens"):
+        pa.decode_attention(q, k, v, bt, ctx[:S - 1], 0.125, 16)
+    with pytest.raises(ValueError, match="out"):
+        pa.decode_attention(q, k, v, bt, ctx, 0.125, 16,
+                            out=torch.zeros((S, Hq - 1, D), dtype=torch.float32))
+    pos = torch.zeros(5, dtype=torch.int32)
+    with pytest.raises(ValueError, match="seq_ids"):
+        pa.compute_slots(bt, pos, bs, NB, seq_ids=torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out"):
+        pa.compute_slots(bt, pos, bs, NB, out=torch.zeros(4, dtype=torch.int64))
+    kn = torch.zeros((5, Hkv, D), dtype=bf)
+    with pytest.raises(ValueError, match="seq_ids"):
+        pa.write_kv_at(k, v, kn, kn, bt, pos, seq_ids=torch.zeros(6, dtype=torch.int32))
+    with pytest.raises(ValueError, match="slots_out"):
+        pa.write_kv_at(k, v, kn, kn, bt, pos, slots_out=torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(ValueError, match="block_mapping"):
+        pa.copy_blocks(k, v, torch.zeros(6, dtype=torch.int32))
+    with pytest.raises(ValueError, match="query_start"):
+        pa.prefill_attention(q, k, v, bt, ctx, torch.zeros(S, dtype=torch.int32), 0.125, 4)
+    with pytest.raises(ValueError, match="out"):
+        pa.prefill_attention(q, k, v, bt, ctx, torch.zeros(S + 1, dtype=torch.int32), 0.125, 4,
+                             out=torch.zeros((S, Hq, D + 1), dtype=torch.float32))

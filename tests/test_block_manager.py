@@ -2,7 +2,7 @@
 pages' own arithmetic.  Host code only: no GPU needed.
 
 Pins (each from a passage of the pages, cited by title and section):
-  * [nalar] "Sisa alokasi tetap ada, tetapi dibatasi ukuran blok": only a
+  * [nalar] "Sisa alokasi dibatasi oleh granularitas blok": only a
     sequence's last block can be partly empty, so its waste is < block_size.
   * [gyaansetu] "The memory problem": reserving 4096 slots for a 300-token
     answer wastes ~93 %; paged allocation wastes only the last block's tail.
