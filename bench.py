@@ -11,19 +11,28 @@ before timing starts.  Each step reads a different one of several identical
 pool copies (together far larger than the 256 MB last-level cache), so no
 step is served from a cache warmed by the previous one.
 
-    python bench.py [--steps K] [--warmup W] [--config 2]
+    python bench.py [--steps K] [--warmup W]
 
-prints ONE JSON line: KV GB/s of the whole step (`value`), seq-steps/s,
-the decode call's roofline fraction (HIP events on the stream it runs on:
-one pair around the timed back-to-back steps when a step is the decode call
-alone, else a pair around each call), the median / p10 / p90 of single
-calls, the achievable rates of the bandwidth probes (a contiguous stream and
-the decode's own K/V gather with no arithmetic; --no-probes skips them) and
-the CPU oracle's rate on a bounded sample.
+prints ONE JSON line.  Its headline is the Llama-3.1-70B-shaped decode batch
+(256 sequences, 64 query / 8 KV heads); `sub_results` holds the
+Llama-3-8B-shaped batch, the shared-prefix batch, the long-context batch and
+the chunked-prefill step, each with its own roofline and CPU baseline.  Per
+workload: KV GB/s of the whole step (`value`), seq-steps/s, the decode
+call's roofline fraction (HIP events on the stream it runs on: one pair
+around the timed back-to-back steps when a step is the decode call alone,
+else a pair around each call), the median / p10 / p90 of single calls, the
+achievable rates of the bandwidth probes (a contiguous stream and the
+decode's own K/V gather with no arithmetic; --no-probes skips them), the
+KV write at scale (the workload's history fill) and the CPU oracle's rate
+on a bounded sample.
+
+    python bench.py --config N
+
+measures workload N (1-5) alone, with the same fields.
 
     python bench.py --workload prefill
 
-measures the chunked-prefill step instead (the chunk's K/V stored with
+measures the chunked-prefill step alone (the chunk's K/V stored with
 pa_write_kv_at, then pa_prefill_attention): useful TFLOP/s of the causal
 attention against the bf16 matrix-core peak.
 
@@ -32,6 +41,15 @@ attention against the bf16 matrix-core peak.
 measures pa_swap_blocks: 8192 blocks (512 MiB of K and V) out to pinned
 host memory and back, against the PCIe 5.0 x16 peak and a contiguous
 torch copy of the same bytes (the DMA engines' rate on this machine).
+
+    python bench.py --workload study
+
+the paging-overhead and block-size study: the 8B- and 70B-shaped batches at
+block sizes 8, 16, 32 and 64, blocks scattered or contiguous, with the
+decode call's time and rate, the tail waste of the last blocks, the waste a
+contiguous per-sequence reservation would leave, the table bytes, and the
+pages' own closed-form figures beside them; one JSON line per case, then a
+markdown table.
 """
 
 from __future__ import annotations
@@ -59,12 +77,21 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["decode", "prefill", "swap"], default="decode",
-                    help="decode step (default), the chunked-prefill step, or block swap")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="workload (default 2: Llama-3-8B-shaped decode)")
+    ap.add_argument("--workload", choices=["decode", "prefill", "swap", "study"],
+                    default="decode",
+                    help="decode step (default), the chunked-prefill step, block swap, or the "
+                         "block-size study")
+    ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="one decode workload alone (default: the 70B-shaped batch as the "
+                         "headline with workloads 2, 4, 5 and the prefill step as sub-results)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="bound on the oracle's timed CPU sample")
+                    help="bound on the oracle's timed CPU sample of the headline workload")
+    ap.add_argument("--sub-cpu-seconds", type=float, default=6.0,
+                    help="bound on the oracle's timed CPU sample of each sub-result")
+    ap.add_argument("--vector-only", action="store_true",
+                    help="decode with the vector-ALU kernel (fixed partitions) instead of the "
+                         "matrix-core kernel, for the A/B of the two")
+    ap.add_argument("--study-reps", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the bandwidth probes (achievable stream / gather rates)")
@@ -174,7 +201,10 @@ def cpu_baseline_prefill(wl, budget_s):
     }
 
 
-def prefill_main(args):
+def prefill_result(args, cpu_seconds):
+    """The chunked-prefill step (pa_write_kv_at of the chunks' K/V, then
+    pa_prefill_attention) timed over rotated pool copies; returns its result
+    object (useful causal TFLOP/s against the bf16 matrix-core peak)."""
     import torch
 
     import workloads as W
@@ -188,16 +218,20 @@ def prefill_main(args):
     npools = max(2, min(8, -(-4 * LLC_BYTES // pool_bytes) + 1))
     dev.add_pool_copies(npools - 1)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     att_ops = [op for op in dev.step_ops if op[0] == "prefill"]
     other_ops = [op for op in dev.step_ops if op[0] != "prefill"]
-    stream = torch.cuda.current_stream()
+    prepared = [(dev.prepare(other_ops, k, stream=stream), dev.prepare(att_ops, k, stream=stream))
+                for k in range(npools)]
 
     def step(k, ev=None):
-        pool = k % npools
-        dev._run(other_ops, pool, record_slots=False)
+        others, att = prepared[k % npools]
+        for c in others:
+            c()
         if ev is not None:
             ev[0].record(stream)
-        dev._run(att_ops, pool)
+        for c in att:
+            c()
         if ev is not None:
             ev[1].record(stream)
 
@@ -219,9 +253,9 @@ def prefill_main(args):
     value = flops / (ms_step * 1e-3) / 1e12
     res = {
         "metric": PREFILL_METRIC,
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "value": round(value, 2), "unit": "TFLOP/s", "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "dtype": wl.dtype, "data": "synthetic",
         "config": {
             "workload": wl.name, "num_seqs": wl.num_seqs,
             "query_tokens": int(wl.query_start[-1]), "num_q_heads": wl.num_q_heads,
@@ -242,8 +276,10 @@ def prefill_main(args):
         },
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, cpu_seconds)
+    del prepared, dev
+    torch.cuda.empty_cache()
+    return res
 
 
 def swap_main(args):
@@ -311,23 +347,29 @@ def swap_main(args):
     print(json.dumps(res), flush=True)
 
 
-def measured_traffic(wl):
-    """HBM bytes per decode call from a committed counter summary
-    (profiles/decode_traffic*.txt) taken on this workload with the decode
-    source as it is now, if there is one (else None)."""
+def measured_traffic(wl, kernel_src="pa_decode.hip"):
+    """HBM bytes per call from a committed counter summary
+    (profiles/*traffic*.txt) taken on this workload with the kernel source as
+    it is now: (bytes, provenance), or (None, None) when no summary matches.
+    The counters are not read in this run; the provenance says where the
+    figure comes from."""
     import glob
     import hashlib
-    src = os.path.join(ROOT, "paged_kv_cache_188_amd", "csrc", "pa_decode.hip")
+    src = os.path.join(ROOT, "paged_kv_cache_188_amd", "csrc", kernel_src)
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "decode_traffic*.txt"))):
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.txt"))):
         kv = {}
         for line in open(path):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
         if kv.get("kernel_source_sha256") == sha and kv.get("workload") == wl.name:
-            return int(kv["traffic_bytes_per_launch"])
-    return None
+            return int(kv["traffic_bytes_per_launch"]), {
+                "from_profile": os.path.relpath(path, ROOT), "kernel_source_sha256": sha[:16],
+                "measured_in_this_run": False,
+                "how": "rocprofv3 TCC_EA0_RDREQ x 128 B and WRITE_SIZE, calibrated on a copy "
+                       "kernel of known size"}
+    return None, None
 
 
 def calibrate_copy(steps):
@@ -448,53 +490,39 @@ def history_write_timing(torch, dev, wl, stream, reps=5):
     return out
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy(args.steps)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(each sequence's blocks live on one GPU; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def decode_result(cid, args, cpu_seconds, separate=False):
+    """One decode workload: the step timed over rotated pool copies, the
+    decode call's roofline, single-call distribution, probes, the step's
+    other calls and the history write timed alone, and the CPU oracle on a
+    bounded sample.  Returns the result object (no driver-level keys)."""
     import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-    if args.workload == "prefill":
-        prefill_main(args)
-        return
-    if args.workload == "swap":
-        swap_main(args)
-        return
+
     import paged_kv_cache_188_amd as pa
     import workloads as W
     from workloads.device import DeviceWorkload
 
-    wl = W.make(args.config)
+    wl = W.make(cid)
     if args.partition is not None:
         wl.partition_size = args.partition
     dev = DeviceWorkload(wl)
+    stream = torch.cuda.current_stream()
     dev.run_setup()
-    hist = history_write_timing(torch, dev, wl, torch.cuda.current_stream())
+    hist = history_write_timing(torch, dev, wl, stream)
     dev.release_setup_inputs()
     pool_bytes = 2 * dev.pools[0][0].numel() * dev.pools[0][0].element_size()
     npools = max(2, min(8, -(-4 * LLC_BYTES // pool_bytes) + 1))
     dev.add_pool_copies(npools - 1)
     torch.cuda.synchronize()
 
-    ops = dev.step_ops if args.separate else dev.step_ops_append
+    ops = dev.step_ops if separate else dev.step_ops_append
     appended = any(kind == "decode_append" for kind, _ in ops)
     decode_ops = [op for op in ops if op[0] in ("decode", "decode_append")]
     other_ops = [op for op in ops if op[0] not in ("decode", "decode_append")]
-    stream = torch.cuda.current_stream()
     # every call validated and marshalled once per pool copy: a step's host
     # work is then a few foreign-function calls, far less than its GPU time,
     # so the stream never runs dry between steps
-    prepared = [dev.prepare(other_ops + decode_ops, k, stream=stream) for k in range(npools)]
+    prepared = [dev.prepare(other_ops + decode_ops, k, stream=stream,
+                            vector_only=args.vector_only) for k in range(npools)]
     n_other = len(other_ops)
     # When the step is the decode call(s) alone, one pair of HIP events spans
     # the K back-to-back steps; otherwise events bracket each step's decode
@@ -543,7 +571,8 @@ def main():
 
     ms_step = wall * 1e3 / args.steps
     workers = pa.decode_streamk_workers(wl.num_seqs, wl.head_dim, wl.block_size,
-                                        wl.partition_size, dev.torch_dtype)
+                                        wl.partition_size, dev.torch_dtype,
+                                        vector_only=args.vector_only)
     call = "pa_decode_attention_append" if appended else "pa_decode_attention"
     if workers > 0:
         decomposition = {"path": "stream-K", "persistent_waves": workers}
@@ -551,8 +580,10 @@ def main():
     else:
         decomposition = {"path": "fixed partitions", "partition_size": pa.decode_partition_size(
             wl.num_seqs, wl.num_kv_heads, wl.block_size, wl.max_context_len, wl.partition_size)}
+        main_k = "decode_valu_kernel" if args.vector_only or wl.dtype != "bf16" \
+            else "decode_mfma_kernel"
         kernel = (f"{call}: " + ("append_kv_kernel + " if appended else "")
-                  + "decode_mfma_kernel + decode_reduce_kernel")
+                  + main_k + " + decode_reduce_kernel")
     if per_call_events:
         dec_ms = [a.elapsed_time(b) for a, b in events]
         dec_avg_ms = sum(dec_ms) / len(dec_ms)
@@ -573,17 +604,16 @@ def main():
             * (2 if wl.dtype == "bf16" else 4)
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
+    traffic, traffic_src = (None, None) if args.vector_only or args.partition is not None \
+        else measured_traffic(wl)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
-        "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
@@ -613,7 +643,8 @@ def main():
             "kernel": kernel,
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(wl),
+            "traffic": traffic,
+            "traffic_source": traffic_src,
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
         },
@@ -635,12 +666,179 @@ def main():
         ach["decode_frac_of_gather"] = round(achieved / ach["gather_gbps"], 4)
         ach["decode_frac_of_stream"] = round(achieved / ach["stream_gbps"], 4)
         res["achievable"] = ach
-    tr = res["roofline"]["traffic"]
-    if tr:
-        res["roofline"]["traffic_gbps"] = round(tr / (dec_avg_ms * 1e-3) / 1e9, 1)
+    if traffic:
+        res["roofline"]["traffic_gbps"] = round(traffic / (dec_avg_ms * 1e-3) / 1e9, 1)
+    del prepared, dev
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, cpu_seconds)
+    return res
+
+
+def _driver_keys(res, args):
+    """The keys of the one-line contract, in front of a result object."""
+    out = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": res["dtype"], "data": res["data"]}
+    out.update({k: v for k, v in res.items() if k not in out})
+    return out
+
+
+def study(args):
+    """Paging overhead and block size, measured with the decode kernels.
+
+    [nalar] "Sisa alokasi dibatasi oleh granularitas blok" trades tail
+    waste (the unused slots of each sequence's last block) against metadata
+    (table entries) as the block size changes, and [nalar] "Kernel attention
+    harus mengikuti block table" notes that walking the table costs
+    something.  For the Llama-3-8B-shaped batch (64 sequences, 32 / 8 heads,
+    contexts uniform in [128, 4096]) and the Llama-3.1-70B-shaped batch (256
+    sequences, 64 / 8 heads, lognormal contexts up to 8192), at block sizes 8,
+    16, 32 and 64, blocks scattered (seeded shuffle) or contiguous: the
+    pa_decode_attention_append call's median time over rotated pool copies,
+    its KV and algorithmic rates, the unused share of the allocated slots,
+    the share a contiguous per-sequence reservation of the maximum length
+    would leave unused ([gininih] "Masalah fragmentasi memori KV Cache
+    konvensional": 60-80 % of the memory wasted that way; [bicarait]
+    "Blueprint Arsitektur 1: Akar Masalah Fragmentasi KV Cache"), and the
+    table bytes the kernel reads.  The pages' own closed-form figures are
+    computed beside them: the 93 % of a 4096-slot reservation left unused by
+    a 300-token request ([gyaansetu] "The memory problem"), and the (N-1)/N
+    prompt-memory saving of N samples sharing one prompt ([bicarait]
+    "Berbagi Memori Fisik")."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_188_amd as pa
+    import workloads as W
+    from workloads.device import DeviceWorkload
+
+    closed = {
+        "reservation_4096_used_300_unused_frac": round((4096 - 300) / 4096, 4),
+        "paged_bs16_used_300_unused_frac": round((math.ceil(300 / 16) * 16 - 300)
+                                                 / (math.ceil(300 / 16) * 16), 4),
+        "shared_prompt_saving_N4": 3 / 4,
+        "shared_prompt_saving_N8": 7 / 8,
+    }
+    print(json.dumps({"closed_forms": closed}), flush=True)
+    stream = torch.cuda.current_stream()
+    shapes = [
+        ("llama3-8b", 2, 64, 32, lambda r: r.integers(128, 4096, size=64, endpoint=True), 4096),
+        ("llama3.1-70b", 3, 256, 64,
+         lambda r: np.clip(np.rint(r.lognormal(math.log(1024), 0.8, size=256)), 16, 8192), 8192),
+    ]
+    rows = []
+    for label, cid, S, hq, draw, max_len in shapes:
+        ctx = draw(np.random.default_rng(np.random.SeedSequence([188, cid]))).astype(np.int32)
+        for bs in (8, 16, 32, 64):
+            for shuffle in (True, False):
+                rng = np.random.default_rng(np.random.SeedSequence([188, cid, bs, int(shuffle)]))
+                wl = W.decode_workload(
+                    f"{label}-decode bs={bs} {'shuffled' if shuffle else 'contiguous'}", W.BF16,
+                    ctx, hq, 8, 128, bs, rng=rng, seed=(188, cid),
+                    max_blocks_per_seq=math.ceil(max_len / bs), shuffle=shuffle)
+                dev = DeviceWorkload(wl)
+                dev.run_setup()
+                dev.release_setup_inputs()
+                pool_bytes = 2 * dev.pools[0][0].numel() * dev.pools[0][0].element_size()
+                npools = max(2, min(8, -(-4 * LLC_BYTES // pool_bytes) + 1))
+                dev.add_pool_copies(npools - 1)
+                calls = [dev.prepare(dev.step_ops_append, k, stream=stream)
+                         for k in range(npools)]
+                for k in range(5):
+                    for c in calls[k % npools]:
+                        c()
+                torch.cuda.synchronize()
+                ev = [(torch.cuda.Event(enable_timing=True),
+                       torch.cuda.Event(enable_timing=True)) for _ in range(args.study_reps)]
+                for k, (a, b) in enumerate(ev):
+                    a.record(stream)
+                    for c in calls[k % npools]:
+                        c()
+                    b.record(stream)
+                torch.cuda.synchronize()
+                med = _pct([a.elapsed_time(b) for a, b in ev], 0.5)
+                blocks = np.ceil(ctx / bs).astype(np.int64)
+                allocated = int((blocks * bs).sum())
+                workers = pa.decode_streamk_workers(wl.num_seqs, wl.head_dim, bs, 0,
+                                                    dev.torch_dtype)
+                row = {
+                    "batch": label, "block_size": bs,
+                    "placement": "shuffled" if shuffle else "contiguous",
+                    "decode_call_us": round(med * 1e3, 2),
+                    "kv_GBps": round(wl.kv_bytes_read() / med / 1e6, 1),
+                    "algorithmic_GBps": round(wl.decode_bytes() / med / 1e6, 1),
+                    "frac_of_8TBps": round(wl.decode_bytes() / med / 1e6 / HBM_PEAK_GBPS, 4),
+                    "path": "stream-K" if workers > 0 else "fixed partitions",
+                    "tail_waste_frac": round(1 - int(ctx.sum()) / allocated, 5),
+                    "reservation_waste_frac": round(1 - int(ctx.sum()) / (S * max_len), 4),
+                    "table_bytes_read": int(4 * blocks.sum()),
+                }
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+                del calls, dev
+                torch.cuda.empty_cache()
+    print("| batch | block size | placement | decode call (us) | KV GB/s | frac of 8 TB/s | "
+          "path | unused slots (paged) | unused slots (reserved max) | table bytes |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['batch']} | {r['block_size']} | {r['placement']} | {r['decode_call_us']} | "
+              f"{r['kv_GBps']} | {r['frac_of_8TBps']} | {r['path']} | "
+              f"{100 * r['tail_waste_frac']:.2f} % | {100 * r['reservation_waste_frac']:.1f} % | "
+              f"{r['table_bytes_read']} |")
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each sequence's blocks live on one GPU; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.workload == "prefill":
+        print(json.dumps(_driver_keys(prefill_result(args, args.cpu_seconds), args)), flush=True)
+        return
+    if args.workload == "swap":
+        swap_main(args)
+        return
+    if args.workload == "study":
+        study(args)
+        return
+    if args.config is not None:
+        res = decode_result(args.config, args, args.cpu_seconds, separate=args.separate)
+        print(json.dumps(_driver_keys(res, args)), flush=True)
+        return
+    # default: the 70B-shaped batch is the headline; the 8B-shaped,
+    # shared-prefix and long-context batches and the chunked-prefill step are
+    # sub-results of the same line, each with its own roofline and baseline
+    head = decode_result(3, args, args.cpu_seconds, separate=args.separate)
+    print(f"[bench] {head['config']['workload']}: {head['roofline']['frac']}", file=sys.stderr,
+          flush=True)
+    subs = {}
+    for cid in (2, 4, 5):
+        r = decode_result(cid, args, args.sub_cpu_seconds, separate=args.separate)
+        subs[r["config"]["workload"]] = r
+        print(f"[bench] {r['config']['workload']}: {r['roofline']['frac']}", file=sys.stderr,
+              flush=True)
+    r = prefill_result(args, args.sub_cpu_seconds)
+    subs[r["config"]["workload"]] = r
+    print(f"[bench] {r['config']['workload']}: {r['roofline']['frac']}", file=sys.stderr,
+          flush=True)
+    out = _driver_keys(head, args)
+    out["sub_results"] = subs
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -154,7 +154,7 @@ class DeviceWorkload:
                                     vector_only=vector_only, stream=stream)
         return self.out
 
-    def prepare(self, ops, pool=0, partition_size=None, stream=None):
+    def prepare(self, ops, pool=0, partition_size=None, stream=None, vector_only=False):
         """Zero-argument callables that issue `ops` on pool copy `pool`, as
         _run does with record_slots=False; the decode calls are validated and
         marshalled here once (pa.PreparedCall), so issuing one costs a single
@@ -170,8 +170,8 @@ class DeviceWorkload:
                 kw = dict(k_new=x["k"], v_new=x["v"]) if kind == "decode_append" else {}
                 calls.append(pa.decode_attention(
                     self.q, k, v, self.tables[table], self.ctx, wl.scale, self.max_ctx,
-                    partition_size=part, workspace=self._ensure_workspace(part, False),
-                    out=self.out, stream=stream, prepare=True, **kw))
+                    partition_size=part, workspace=self._ensure_workspace(part, vector_only),
+                    out=self.out, stream=stream, prepare=True, vector_only=vector_only, **kw))
             elif kind == "write":
                 calls.append(pa.write_kv_at(k, v, x["k"], x["v"], self.tables[x["table"]],
                                             x["positions"], seq_ids=x["seq_ids"],
