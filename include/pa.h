@@ -32,7 +32,9 @@
  * Pointers.  Every array argument is a DEVICE pointer on the current HIP
  *   device.  The caller allocates and owns all memory, including the decode
  *   workspace; the library allocates nothing and keeps no pointer after the
- *   call returns.  Pools are updated in place.
+ *   call returns (its one static device array, the workspace of
+ *   pa_decode_attention_noalloc, is part of the loaded code).  Pools are
+ *   updated in place.
  * Streams.  `stream` is a hipStream_t passed as void*; NULL is the null
  *   stream.  Every call only enqueues work and returns; results are visible
  *   in stream order.  Ordering between calls (write -> attend, copy -> attend)
@@ -340,6 +342,40 @@ pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache,
                                      int32_t partition_size, void* workspace,
                                      size_t workspace_bytes, pa_dtype dtype,
                                      uint32_t flags, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode_attention_noalloc  (decode with no allocation and no workspace)
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  With k_new
+ * and v_new given it is pa_decode_attention_append, with both NULL it is
+ * pa_decode_attention; arguments, results, decomposition and determinism are
+ * exactly theirs, except that there is no workspace argument: the partials
+ * live in a static device array of PA_NOALLOC_MAX_WORKSPACE bytes that the
+ * library holds on every GPU it runs on until the process ends.  A call
+ * whose workspace (pa_decode_workspace_size for the same arguments) exceeds
+ * that returns PA_ERR_WORKSPACE before anything is launched; the stream-K
+ * path of every supported shape fits.  The call allocates nothing (no
+ * hipMalloc or other allocating routine); the first call on a device looks
+ * up the array's device address once.  All calls on one GPU share the array
+ * and its contents between calls are unspecified: calls that may overlap on
+ * one GPU (different streams, or host threads) race and must be ordered by
+ * the caller.  One of k_new / v_new NULL without the other: PA_ERR_NULL.
+ * ------------------------------------------------------------------------- */
+#define PA_NOALLOC_MAX_WORKSPACE ((size_t)34 << 20)
+
+pa_status pa_decode_attention_noalloc(float* out, const void* q, void* k_cache,
+                                      void* v_cache, const void* k_new,
+                                      const void* v_new, int64_t new_token_stride,
+                                      const int32_t* block_tables,
+                                      const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq,
+                                      int32_t max_context_len, float scale,
+                                      int32_t partition_size, pa_dtype dtype,
+                                      uint32_t flags, void* stream);
 
 /* ---------------------------------------------------------------------------
  * pa_prefill_attention  (multi-query paged attention: a prompt chunk)

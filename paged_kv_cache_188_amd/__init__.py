@@ -26,6 +26,7 @@ LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(
 PA_F32 = 0
 PA_BF16 = 1
 PA_DECODE_VECTOR_ONLY = 1
+PA_NOALLOC_MAX_WORKSPACE = 34 << 20  # bytes (include/pa.h)
 
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
           4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CAPACITY"}
@@ -83,6 +84,10 @@ SIGNATURES = {
                                                   _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                   ctypes.c_float, _I32, _P, ctypes.c_size_t,
                                                   ctypes.c_int, ctypes.c_uint32, _P]),
+    "pa_decode_attention_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I32,
+                                                   _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                   ctypes.c_float, _I32, ctypes.c_int,
+                                                   ctypes.c_uint32, _P]),
     "pa_prefill_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                             _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
                                             ctypes.c_int, _P]),
@@ -405,6 +410,48 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max
                 float(scale), int(partition_size)) + ws + tail
     call = PreparedCall(name, args, keep, out)
     return call if prepare else call()
+
+
+def decode_attention_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale,
+                             max_context_len, partition_size=0, out=None, vector_only=False,
+                             stream=None, k_new=None, v_new=None):
+    """decode_attention (k_new/v_new None) or its append form, through
+    pa_decode_attention_noalloc: no workspace argument and nothing allocated
+    by the library (``out`` is allocated here when not given).  Calls on one
+    GPU share the library's static workspace and must not overlap."""
+    import torch
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [S][Hq][D] and block_tables [S][MB]")
+    s, hq, d = q.shape
+    mb = block_tables.shape[1]
+    _shape(context_lens, (s,), "context_lens")
+    _shape(out, (s, hq, d), "out")
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
+    if d2 != d:
+        raise ValueError("q and the pools disagree in head_dim")
+    _need(q, k_cache.dtype, "q")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    if (k_new is None) != (v_new is None):
+        raise TypeError("give both k_new and v_new, or neither")
+    stride = 0
+    if k_new is not None:
+        if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+            raise TypeError("k_new and v_new must have the pool's element type")
+        if k_new.shape != (s, hkv, d) or v_new.shape != k_new.shape:
+            raise ValueError("k_new/v_new must be [S][Hkv][D]")
+        if k_new.stride(2) != 1 or k_new.stride(1) != d or v_new.stride() != k_new.stride():
+            raise ValueError("k_new/v_new rows must be contiguous [Hkv][D] with one token stride")
+        stride = k_new.stride(0)
+    if out is None:
+        out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    _check("pa_decode_attention_noalloc", lib().pa_decode_attention_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), stride,
+        _ptr(block_tables), _ptr(context_lens), s, hq, hkv, d, bs, nb, mb, int(max_context_len),
+        float(scale), int(partition_size), _dtype_code(k_cache),
+        PA_DECODE_VECTOR_ONLY if vector_only else 0, _stream(stream)))
+    return out
 
 
 def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,

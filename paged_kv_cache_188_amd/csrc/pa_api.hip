@@ -8,6 +8,16 @@
 
 #include "pa_internal.h"
 
+// Workspace of pa_decode_attention_noalloc: file-scope device memory, one
+// copy per GPU the library runs on, held until the process ends.  Its size,
+// PA_NOALLOC_MAX_WORKSPACE, covers the stream-K workspace of every supported
+// shape (2048 wave slots x 2 partials x 16 heads x (128 + 2) floats, plus
+// the hand-off entries) and fixed-partition workspaces up to the same size.
+// Nothing in it has to start at zero: every entry a kernel reads was written
+// earlier in the same call.  In host code `scratch` is only a handle, never a
+// device address; the address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_MAX_WORKSPACE];
+
 namespace {
 
 bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
@@ -72,6 +82,23 @@ int streamk_workers(int head_dim, int* out) {
   if (dev < kMaxDevices) cache[dev][k].store((int)w, std::memory_order_relaxed);
   *out = (int)w;
   return 0;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (nullptr on a HIP error).
+void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  addr[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 }  // namespace
@@ -280,7 +307,7 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                       int32_t max_context_len, float scale, int32_t partition_size,
                       void* workspace, size_t workspace_bytes, pa_dtype dtype, uint32_t flags,
-                      bool append, void* stream) {
+                      bool append, bool static_scratch, void* stream) {
   if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1 || max_context_len < 0 || num_q_heads % num_kv_heads)
@@ -313,8 +340,12 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
       path == pa::DecodePath::kStreamK
           ? pa::decode_workspace_streamk(num_seqs, num_q_heads / num_kv_heads, head_dim)
           : pa::decode_workspace_partition(num_seqs, num_q_heads, head_dim, (int)P);
-  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PA_ERR_WORKSPACE;
-  if (ws.total > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PA_ERR_WORKSPACE;
+  if (static_scratch) {
+    if (ws.total > PA_NOALLOC_MAX_WORKSPACE) return PA_ERR_WORKSPACE;
+  } else {
+    if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return PA_ERR_WORKSPACE;
+    if (ws.total > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PA_ERR_WORKSPACE;
+  }
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_UNSUPPORTED;
@@ -326,6 +357,10 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
     if ((new_token_stride * e) % 16) return PA_ERR_UNSUPPORTED;
     if (!k_new || !v_new) return PA_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_UNSUPPORTED;
+  }
+  if (static_scratch && ws.total > 0) {  // validation done: the first HIP call
+    workspace = noalloc_scratch();
+    if (!workspace) return PA_ERR_HIP;
   }
 
   pa::DecodeParams p{};
@@ -391,7 +426,7 @@ pa_status pa_decode_attention(float* out, const void* q, const void* k_cache, co
   return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, 0, block_tables, context_lens,
                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
-                     workspace_bytes, dtype, flags, false, stream);
+                     workspace_bytes, dtype, flags, false, false, stream);
 }
 
 pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache, void* v_cache,
@@ -407,7 +442,23 @@ pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache, v
   return decode_impl(out, q, k_cache, v_cache, k_new, v_new, new_token_stride, block_tables,
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
-                     workspace, workspace_bytes, dtype, flags, true, stream);
+                     workspace, workspace_bytes, dtype, flags, true, false, stream);
+}
+
+pa_status pa_decode_attention_noalloc(float* out, const void* q, void* k_cache, void* v_cache,
+                                      const void* k_new, const void* v_new,
+                                      int64_t new_token_stride, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, int32_t partition_size, pa_dtype dtype,
+                                      uint32_t flags, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+  return decode_impl(out, q, k_cache, v_cache, k_new, v_new, new_token_stride, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
+                     nullptr, 0, dtype, flags, k_new != nullptr, true, stream);
 }
 
 pa_status pa_prefill_attention(float* out, const void* q, const void* k_cache,

@@ -336,3 +336,32 @@ def test_binding_checks_buffer_shapes_before_any_call():
     with pytest.raises(ValueError, match="out"):
         pa.prefill_attention(q, k, v, bt, ctx, torch.zeros(S + 1, dtype=torch.int32), 0.125, 4,
                              out=torch.zeros((S, Hq, D + 1), dtype=torch.float32))
+
+
+def test_noalloc_validation(lib):
+    """pa_decode_attention_noalloc validates like the workspace calls and
+    refuses, before any HIP call, a decomposition whose workspace exceeds its
+    static array."""
+    na = lambda **k: lib.pa_decode_attention_noalloc(
+        k.get("out", FAKE), FAKE, FAKE, FAKE, k.get("kn", FAKE), k.get("vn", FAKE),
+        k.get("stride", 0), FAKE, FAKE, k.get("S", 2), 8, 2, 128, 16, 10, k.get("MB", 4),
+        k.get("max_ctx", 40), 0.1, k.get("part", 64), k.get("dtype", 1), k.get("flags", 0),
+        NULL)
+    assert na(dtype=5) == DTYPE
+    assert na(kn=NULL) == NUL                  # one of the new-row pointers without the other
+    assert na(vn=NULL) == NUL
+    assert na(out=NULL) == NUL
+    assert na(stride=100) == SHAPE
+    assert na(flags=4) == UNSUP
+    assert na(S=0, out=NULL) == OK
+    # 16-token partitions over a declared 2^20-token context: more partials
+    # than the static array holds
+    need = lib.pa_decode_workspace_size(2, 8, 2, 128, 16, 1 << 20, 16, 1, 0)
+    assert need > pa.PA_NOALLOC_MAX_WORKSPACE
+    assert na(part=16, max_ctx=1 << 20, MB=1 << 16) == WS
+
+
+def test_noalloc_limit_matches_header():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    m = re.search(r"#define PA_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.PA_NOALLOC_MAX_WORKSPACE
