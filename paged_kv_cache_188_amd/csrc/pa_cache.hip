@@ -136,26 +136,41 @@ __global__ __launch_bounds__(kWriteWaves * kWave) void write_kv_at_kernel(
               num_kv_heads, head_chunks, lane);
 }
 
-// Tokens are taken 16 at a time, one workgroup of four waves per group
-// (workgroups renumbered with xcd_run).  The K rows of the group are staged
-// in LDS, so that the loads read whole token rows and the stores write, for
-// each (head, granule), the 16 tokens' granules with 16 consecutive threads:
-// when the tokens sit at consecutive offsets of a block (a prompt chunk or a
-// history written in order) those granules are one contiguous 256-byte run
-// of the K pool.  V rows go straight through (a token's row is contiguous in
-// the V pool).  Every token is stored at its own slot, so any slot pattern
-// is handled; tokens with no slot (padding, outside the table or the pool)
-// are skipped.  Rows wider than the LDS staging (more than kRunMaxChunks
-// granules) take a per-token path, each wave four tokens with all their
+// Large writes: each workgroup of four waves owns a window of 8 tokens
+// (windows renumbered with xcd_run), and the K rows are staged in LDS so the
+// stores can be laid out by line.  A K pool line (128 bytes) holds one
+// 16-byte granule of 8 consecutive slots of a block (slots 8a .. 8a+7 of one
+// (block, head, granule)), and the 8 tokens whose slots those are are usually
+// consecutive in the write (a prompt chunk or a history written in order),
+// but a window of tokens need not start at such a line boundary.  So the
+// tokens are cut into RUNS: a token continues the run of the token before it
+// when its slot is the next slot and not the first of a line; otherwise it
+// leads a run.  A workgroup stores the runs whose leader lies in its window,
+// whole, even when they reach up to 7 tokens into the next window, and skips
+// the tokens at the start of its window that continue a run led before it.
+// Every line written by consecutive tokens is then written by one workgroup
+// in one piece, with streaming stores when its 8 slots are all written
+// (ordinary stores for a part of a line, so L2 can still merge it with
+// another workgroup's part).  Every token is still stored at exactly its
+// own slot by exactly one workgroup, so any slot pattern is handled; tokens
+// with no slot (padding, outside the table or the pool) are skipped.  V rows
+// are whole lines (a token's row per head) and go straight through.  Rows
+// wider than the LDS staging (more than kRunMaxChunks granules) take a
+// per-token path over the window, each wave two tokens with all their
 // loads issued before their stores.
-constexpr int kRunTokens = 16;
-constexpr int kRunThreads = kWriteWaves * kWave;
-// LDS staging: 16 tokens x (nchunks + 1) granules, kept under 64 KiB
-constexpr int kRunMaxChunks = 240;
+constexpr int kRunTokens = 8;                     // tokens per window
+constexpr int kRunLine = 8;                       // slots per K line
+constexpr int kRunOwned = kRunTokens + kRunLine - 1;  // most tokens a workgroup stores
+constexpr int kRunWaves = kWriteWaves;
+constexpr int kRunThreads = kRunWaves * kWave;
+// LDS staging: kRunOwned tokens x (nchunks + 1) granules, kept under 64 KiB
+constexpr int kRunMaxChunks = 64 * 1024 / (16 * kRunOwned) - 1;
 // Fewer tokens than this (a decode step's one token per sequence) go one
 // wave per token instead: the latency of a small write is lower that way
 // (64 tokens: ~4 us against ~6 us staged), and there are no runs to gain.
 constexpr int kRunMinTokens = 1024;
+constexpr int kRunWaveTokens = kRunTokens / kRunWaves;  // per-token path: tokens per wave
+static_assert(kRunTokens % kRunWaves == 0, "the per-token path splits a window over the waves");
 
 __global__ __launch_bounds__(kRunThreads) void write_kv_runs_kernel(
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
@@ -165,43 +180,82 @@ __global__ __launch_bounds__(kRunThreads) void write_kv_runs_kernel(
     const int32_t* __restrict__ positions, int64_t* __restrict__ slots_out, int num_tokens,
     int64_t token_stride_bytes, int num_blocks, int block_size, int num_kv_heads,
     int head_chunks) {
-  extern __shared__ uint4 s_k[];  // [16][nchunks + 1] granules
-  // byte offsets of granule 0 of each token's K and V rows in the pools, or -1
-  __shared__ int64_t s_kbase[kRunTokens], s_vbase[kRunTokens];
+  extern __shared__ uint4 s_k[];  // [kRunOwned][nchunks + 1] granules
+  // slots of tokens j0-1 .. j0+kRunOwned-1 (entry t is token j0-1+t), then
+  // the owned tokens: their index (relative to j0), slot and run length
+  __shared__ int64_t s_slot[kRunOwned + 1];
+  __shared__ int s_tok[kRunOwned];
+  __shared__ int64_t s_own_slot[kRunOwned];
+  __shared__ int s_run_len[kRunOwned];
+  __shared__ int s_owned;
   const int tid = threadIdx.x;
   const int j0 = xcd_run(blockIdx.x, gridDim.x) * kRunTokens;
   const int64_t pool_slots = (int64_t)num_blocks * block_size;
-  if (tid < kRunTokens) {
-    const int j = j0 + tid;
+  const int nchunks = num_kv_heads * head_chunks;  // granules per token row
+  const bool staged = nchunks <= kRunMaxChunks;
+  const int span = staged ? kRunOwned + 1 : kRunTokens + 1;
+  if (tid < span) {
+    const int j = j0 - 1 + tid;
     int64_t slot = -1;
-    if (j < num_tokens) {
+    if (j >= 0 && j < num_tokens) {
       if (slot_mapping) {
         slot = slot_mapping[j];
         if (slot >= pool_slots) slot = -1;  // outside the pool: skipped
       } else {
         slot = token_slot(block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions, j,
                           block_size, num_blocks);
-        if (slots_out) slots_out[j] = slot;
+        if (slots_out && tid >= 1 && tid <= kRunTokens) slots_out[j] = slot;
       }
+      if (slot < 0) slot = -1;
     }
-    int64_t kb = -1, vb = -1;
-    if (slot >= 0) {
-      const int64_t blk = slot / block_size, off = slot - blk * block_size;
-      // K element (h, granule w) at ((blk*Hkv + h)*hc + w)*bs + off; V at
-      // ((blk*Hkv + h)*bs + off)*hc + w (granules of 16 bytes)
-      kb = (blk * num_kv_heads * head_chunks * block_size + off) * 16;
-      vb = (blk * num_kv_heads * block_size + off) * head_chunks * 16;
-    }
-    s_kbase[tid] = kb;
-    s_vbase[tid] = vb;
+    s_slot[tid] = slot;
   }
   __syncthreads();
-  const int nchunks = num_kv_heads * head_chunks;  // granules per token row
   const int64_t vhead = (int64_t)block_size * head_chunks * 16;  // V bytes per (block, head)
   const int64_t kgran = (int64_t)block_size * 16;                // K bytes per (block, head, granule)
-  if (nchunks <= kRunMaxChunks) {
+  // byte offsets of granule 0 of a slot's K and V rows in the pools
+  auto kbase = [&](int64_t slot) {
+    const int64_t blk = slot / block_size, off = slot - blk * block_size;
+    return (blk * num_kv_heads * head_chunks * block_size + off) * 16;
+  };
+  auto vbase = [&](int64_t slot) {
+    const int64_t blk = slot / block_size, off = slot - blk * block_size;
+    return (blk * num_kv_heads * block_size + off) * head_chunks * 16;
+  };
+  if (staged) {
+    if (tid < kWave) {
+      // ownership, in the first wave: lane t holds token j0-1+t; a token
+      // continues a run when its slot is the previous token's plus one and
+      // not the first of a line
+      const int64_t sl = tid <= kRunOwned ? s_slot[tid] : -1;
+      const int64_t prev = tid >= 1 && tid <= kRunOwned ? s_slot[tid - 1] : -1;
+      const bool cont = tid >= 1 && sl >= 0 && prev >= 0 && sl == prev + 1 &&
+                        sl % kRunLine != 0;
+      // leaders: every lane that does not continue (lane 0, the token
+      // before the window, and lanes past the staging range included)
+      const uint64_t lead = __ballot(!cont);
+      const int t = tid;
+      // the run's leader: the highest leading lane <= t; its end: the lowest
+      // leading lane > t (lane kRunOwned + 1 always leads)
+      const uint64_t upto = t == 63 ? ~0ull : ((2ull << t) - 1);
+      const int first = 63 - __builtin_clzll(lead & upto);
+      const uint64_t above = t == 63 ? 0ull : (lead & ~upto);
+      const int next = above ? __builtin_ctzll(above) : 64;
+      const bool own = t >= 1 && t <= kRunOwned && sl >= 0 && first >= 1 &&
+                       first <= kRunTokens;
+      const uint64_t owned_mask = __ballot(own);
+      if (own) {
+        const int n = __builtin_popcountll(owned_mask & ((1ull << t) - 1));
+        s_tok[n] = t - 1;
+        s_own_slot[n] = sl;
+        s_run_len[n] = next - first;
+      }
+      if (tid == 0) s_owned = __builtin_popcountll(owned_mask);
+    }
+    __syncthreads();
+    const int owned = s_owned;
     const int row = nchunks + 1;  // padded LDS row: the transposed reads hit distinct banks
-    const int total = kRunTokens * nchunks;
+    const int total = owned * nchunks;
     // eight granules of K and of V per thread in flight: all loads of a batch
     // are issued before any of them is stored
     constexpr int kBatch = 8;
@@ -212,8 +266,8 @@ __global__ __launch_bounds__(kRunThreads) void write_kv_runs_kernel(
         const int e = e0 + u * kRunThreads;
         const int i = e / nchunks, c = e - i * nchunks;
         kx[u] = vx[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (e < total && s_vbase[i] >= 0) {
-          const int64_t src = (int64_t)(j0 + i) * token_stride_bytes + (int64_t)c * 16;
+        if (e < total) {
+          const int64_t src = (int64_t)(j0 + s_tok[i]) * token_stride_bytes + (int64_t)c * 16;
           kx[u] = *reinterpret_cast<const uint4*>(k_new + src);
           vx[u] = *reinterpret_cast<const uint4*>(v_new + src);
         }
@@ -222,55 +276,50 @@ __global__ __launch_bounds__(kRunThreads) void write_kv_runs_kernel(
       for (int u = 0; u < kBatch; ++u) {
         const int e = e0 + u * kRunThreads;
         const int i = e / nchunks, c = e - i * nchunks;
-        if (e < total && s_vbase[i] >= 0) {
+        if (e < total) {
           s_k[i * row + c] = kx[u];
           const int h = c / head_chunks, w = c - h * head_chunks;
-          store_stream(v_cache + s_vbase[i] + h * vhead + w * 16, vx[u]);
+          store_stream(v_cache + vbase(s_own_slot[i]) + h * vhead + w * 16, vx[u]);
         }
       }
     }
     __syncthreads();
-    // Whole runs (the 16 tokens at offsets 16m .. 16m+15 of one block) are
-    // streamed; partial runs use ordinary stores, so that L2 merges them with
-    // the neighbouring group's part of the same lines (written by the same
-    // XCD, see xcd_run) before write-back.
-    bool whole = s_kbase[0] >= 0 && block_size % kRunTokens == 0 &&
-                 (s_kbase[0] / 16) % kRunTokens == 0;
-#pragma unroll
-    for (int i = 1; i < kRunTokens; ++i) whole = whole && s_kbase[i] == s_kbase[0] + 16 * i;
-    for (int e = tid; e < kRunTokens * nchunks; e += kRunThreads) {
-      const int c = e / kRunTokens, i = e - c * kRunTokens;  // (head, granule) c, token i
-      const int64_t kb = s_kbase[i];
-      if (kb < 0) continue;
-      if (whole)
-        store_stream(k_cache + kb + c * kgran, s_k[i * row + c]);
+    // K: for each (head, granule) c, the owned tokens' granules by
+    // consecutive threads, so a run's granules are one contiguous piece of a
+    // line; a run of kRunLine tokens fills its line and is streamed
+    for (int e = tid; e < owned * nchunks; e += kRunThreads) {
+      const int c = e / owned, i = e - c * owned;
+      uint8_t* dst = k_cache + kbase(s_own_slot[i]) + c * kgran;
+      if (s_run_len[i] == kRunLine)
+        store_stream(dst, s_k[i * row + c]);
       else
-        *reinterpret_cast<uint4*>(k_cache + kb + c * kgran) = s_k[i * row + c];
+        *reinterpret_cast<uint4*>(dst) = s_k[i * row + c];
     }
     return;
   }
-  // per-token path: wave v takes tokens j0 + 4v .. j0 + 4v + 3
+  // per-token path over the window: wave v takes its kRunWaveTokens tokens
   const int wave = tid / kWave, lane = tid % kWave;
+  const int t0 = kRunWaveTokens * wave;
   for (int c = lane; c < nchunks; c += kWave) {
     const int h = c / head_chunks, w = c - h * head_chunks;
-    uint4 a[4], b[4];
+    uint4 a[kRunWaveTokens], b[kRunWaveTokens];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < kRunWaveTokens; ++t) {
       a[t] = b[t] = make_uint4(0u, 0u, 0u, 0u);
-      if (s_vbase[4 * wave + t] < 0) continue;
-      const int64_t src = (int64_t)(j0 + 4 * wave + t) * token_stride_bytes + (int64_t)c * 16;
+      if (s_slot[1 + t0 + t] < 0) continue;
+      const int64_t src = (int64_t)(j0 + t0 + t) * token_stride_bytes + (int64_t)c * 16;
       a[t] = *reinterpret_cast<const uint4*>(k_new + src);
       b[t] = *reinterpret_cast<const uint4*>(v_new + src);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t kb = s_kbase[4 * wave + t], vb = s_vbase[4 * wave + t];
-      if (vb < 0) continue;
+    for (int t = 0; t < kRunWaveTokens; ++t) {
+      const int64_t slot = s_slot[1 + t0 + t];
+      if (slot < 0) continue;
       // K granules of consecutive tokens of a block share lines, which
       // ordinary stores let L2 merge before write-back; a V row is whole
       // lines, streamed
-      *reinterpret_cast<uint4*>(k_cache + kb + c * kgran) = a[t];
-      store_stream(v_cache + vb + h * vhead + w * 16, b[t]);
+      *reinterpret_cast<uint4*>(k_cache + kbase(slot) + c * kgran) = a[t];
+      store_stream(v_cache + vbase(slot) + h * vhead + w * 16, b[t]);
     }
   }
 }
@@ -343,7 +392,7 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
     return hipGetLastError();
   }
   const int nchunks = num_kv_heads * (head_bytes / 16);
-  const size_t lds = nchunks <= kRunMaxChunks ? (size_t)kRunTokens * (nchunks + 1) * 16 : 0;
+  const size_t lds = nchunks <= kRunMaxChunks ? (size_t)kRunOwned * (nchunks + 1) * 16 : 0;
   hipLaunchKernelGGL(write_kv_runs_kernel, dim3((num_tokens + kRunTokens - 1) / kRunTokens),
                      dim3(kRunThreads), lds, stream, static_cast<uint8_t*>(k_cache),
                      static_cast<uint8_t*>(v_cache), static_cast<const uint8_t*>(k_new),
@@ -409,7 +458,7 @@ hipError_t launch_write_kv_at(void* k_cache, void* v_cache, const void* k_new, c
     return hipGetLastError();
   }
   const int nchunks = num_kv_heads * (head_bytes / 16);
-  const size_t lds = nchunks <= kRunMaxChunks ? (size_t)kRunTokens * (nchunks + 1) * 16 : 0;
+  const size_t lds = nchunks <= kRunMaxChunks ? (size_t)kRunOwned * (nchunks + 1) * 16 : 0;
   hipLaunchKernelGGL(write_kv_runs_kernel, dim3((num_tokens + kRunTokens - 1) / kRunTokens),
                      dim3(kRunThreads), lds, stream, static_cast<uint8_t*>(k_cache),
                      static_cast<uint8_t*>(v_cache), static_cast<const uint8_t*>(k_new),

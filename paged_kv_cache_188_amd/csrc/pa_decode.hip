@@ -692,7 +692,18 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
     }
     return;
   }
-  const int64_t w1 = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs in turn, so the decode kernel's
+  // workgroup b (waves 4b .. 4b+3) ran on XCD b mod 8.  When the decode grid
+  // is a multiple of 8 workgroups, merge workgroup m takes a wave slot whose
+  // decode workgroup ran on m's own XCD, m mod 8: the hand-off entry and the
+  // partials written there (and those of the neighbouring waves of the same
+  // workgroup) can still be in that XCD's L2.
+  const int nb = p.max_workers / kDecodeWaves;
+  int64_t w1 = blockIdx.x;
+  if (nb % 8 == 0) {
+    const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+    w1 = (int64_t)(8 * (k / kDecodeWaves) + x) * kDecodeWaves + k % kDecodeWaves;
+  }
   const int2 h = reinterpret_cast<const int2*>(p.ws_handoff)[w1];
   if (h.x < 0) return;
   const int seq = h.x / p.num_kv_heads, kvh = h.x % p.num_kv_heads;
