@@ -54,6 +54,14 @@
 // layout; the vector-ALU trims -- uniform base addresses, three-way max, V
 // zeroing on one step, transposing V loads instead of byte permutes -- took
 // a further 17 %.)
+// Occupancy: K operands are read from LDS one 32-dim slice at a time and V
+// operands one output tile at a time, right before their MFMAs, which keeps
+// the kernel at 168 registers: three workgroups per CU (three waves per
+// SIMD) instead of two; the waves raise their priority while they issue
+// matrix-core work (s_setprio), so a SIMD's matrix core is fed first.
+// (Measured: 417 -> 397 us with three workgroups per CU, -> 388 us with the
+// priority; interleaving one row half's P V with the other half's softmax
+// inside a wave, or one barrier per two steps, gained nothing.)
 // Scheduling: the work of a (sequence, query tile) pair is its number of key
 // steps, known only from device data.  Each workgroup first ranks all pairs
 // by decreasing work (a bucketed counting sort in LDS, the same in every
@@ -246,7 +254,7 @@ __device__ int longest_first_pair(const DecodeParams& p, const int32_t* query_st
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
+__global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
     const DecodeParams p, const int32_t* __restrict__ query_start, int64_t total_q, int tq,
     int qtiles, int64_t n_items) {
   static_assert(BS >= 16 && BS % 16 == 0, "16-key halves lie in one block");
@@ -383,42 +391,37 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
     // S^T = K Q^T: sc[half][row half]; all K operands first, then the four
     // accumulations interleaved
     f32x4_t sc[2][2];
-    {
-      bf16x8_t a[2][NS];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sc[kh][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);  // matrix-core phase: issue ahead of the vector work
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bf16x8_t a[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) a[kh] = as_bf16x8(buf[kh * HALF + (4 * s + grp) * 16 + col]);
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int s = 0; s < NS; ++s) a[kh][s] = as_bf16x8(buf[kh * HALF + (4 * s + grp) * 16 + col]);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) sc[kh][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            sc[kh][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kh][s], qv[h][s], sc[kh][h], 0, 0, 0);
+        for (int h = 0; h < 2; ++h)
+          sc[kh][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kh], qv[h][s], sc[kh][h], 0, 0, 0);
     }
     // B operands of P V, read before the softmax so the loads overlap it.
     // Dim tile nt: lane (grp, n) holds V at keys 4*grp + j and 16 + 4*grp + j
     // (j = 0..3; the order of P's elements) and dim 16*nt + n, read with two
     // transposing LDS loads: source lane 4*j + r of a 16-lane group supplies
     // key 4*grp + j (+16), dims 16*nt + 4*r .. +3
-    bf16x8_t bv[DV];
-    {
-      const char* vl = reinterpret_cast<const char*>(buf + 2 * HALF) + vlane;
-#pragma unroll
-      for (int nt = 0; nt < DV; ++nt) {
-        const v4s_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(vl + nt * 32));
-        const v4s_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(vl + 16 * VRS * 16 + nt * 32));
-        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo4), h2 = __builtin_bit_cast(u32x2_t, hi4);
-        bv[nt] = as_bf16x8(u32x4_t{l2.x, l2.y, h2.x, h2.y});
-      }
-    }
+    const char* vl = reinterpret_cast<const char*>(buf + 2 * HALF) + vlane;
+    auto vop = [&](int nt) {
+      const v4s_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s_t*)(vl + nt * 32));
+      const v4s_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s_t*)(vl + 16 * VRS * 16 + nt * 32));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo4), h2 = __builtin_bit_cast(u32x2_t, hi4);
+      return as_bf16x8(u32x4_t{l2.x, l2.y, h2.x, h2.y});
+    };
+    __builtin_amdgcn_s_setprio(0);
     // softmax: exponent arguments s * c - m (the causal mask only on steps
     // that reach past some row's position), lazy reference point, P split
     const bool diag = step * kStep + kStep - 1 > wmin;
@@ -469,21 +472,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_flash_kernel(
       l_run[h] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
       split_weights(pw, phi[h], plo[h]);
     }
-    // O += P V: eight independent accumulations between two on the same
-    // accumulator
+    // O += P V, V's operand of each output tile read just before its four MFMAs
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int n0 = 0; n0 < DV; n0 += 4) {
+    for (int nt = 0; nt < DV; ++nt) {
+      const bf16x8_t b = vop(nt);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[h][n0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[h], bv[n0 + t], acc[h][n0 + t], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[h][n0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[h], bv[n0 + t], acc[h][n0 + t], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        acc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[h], b, acc[h][nt], 0, 0, 0);
+        acc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[h], b, acc[h][nt], 0, 0, 0);
+      }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // normalise and store: acc[h][nt][r] is row wave*32 + 16h + 4*grp + r,
