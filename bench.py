@@ -15,8 +15,10 @@ step is served from a cache warmed by the previous one.
 
 prints ONE JSON line.  Its headline is the Llama-3.1-70B-shaped decode batch
 (256 sequences, 64 query / 8 KV heads); `sub_results` holds the
-Llama-3-8B-shaped batch, the shared-prefix batch, the long-context batch and
-the chunked-prefill step, each with its own roofline and CPU baseline.  Per
+Llama-3-8B-shaped batch, the shared-prefix batch (through the plain call and
+through pa_decode_attention_shared, which reads each shared block once per
+group of samples), the long-context batch and the chunked-prefill step, each
+with its own roofline and CPU baseline.  Per
 workload: KV GB/s of the whole step (`value`), seq-steps/s, the decode
 call's roofline fraction (HIP events on the stream it runs on: one pair
 around the timed back-to-back steps when a step is the decode call alone,
@@ -28,7 +30,8 @@ on a bounded sample.
 
     python bench.py --config N
 
-measures workload N (1-5) alone, with the same fields.
+measures workload N (1-5) alone, with the same fields; with --shared its
+decode runs through pa_decode_attention_shared.
 
     python bench.py --workload prefill
 
@@ -99,6 +102,9 @@ def parse():
                     help="decode partition size (default: the workload's / the library's choice)")
     ap.add_argument("--separate", action="store_true",
                     help="store the new tokens with pa_write_kv_at, then pa_decode_attention")
+    ap.add_argument("--shared", action="store_true",
+                    help="run the decode through pa_decode_attention_shared (groups of "
+                         "sequences that share prefix blocks read them once)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run pa_copy_blocks over a known number of bytes (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -347,7 +353,7 @@ def swap_main(args):
     print(json.dumps(res), flush=True)
 
 
-def measured_traffic(wl, kernel_src="pa_decode.hip"):
+def measured_traffic(wl, kernel_src="pa_decode.hip", call=None):
     """HBM bytes per call from a committed counter summary
     (profiles/*traffic*.txt) taken on this workload with the kernel source as
     it is now: (bytes, provenance), or (None, None) when no summary matches.
@@ -363,7 +369,8 @@ def measured_traffic(wl, kernel_src="pa_decode.hip"):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        if kv.get("kernel_source_sha256") == sha and kv.get("workload") == wl.name:
+        if (kv.get("kernel_source_sha256") == sha and kv.get("workload") == wl.name
+                and kv.get("call") == call):
             return int(kv["traffic_bytes_per_launch"]), {
                 "from_profile": os.path.relpath(path, ROOT), "kernel_source_sha256": sha[:16],
                 "measured_in_this_run": False,
@@ -490,11 +497,14 @@ def history_write_timing(torch, dev, wl, stream, reps=5):
     return out
 
 
-def decode_result(cid, args, cpu_seconds, separate=False):
+def decode_result(cid, args, cpu_seconds, separate=False, shared=False):
     """One decode workload: the step timed over rotated pool copies, the
     decode call's roofline, single-call distribution, probes, the step's
     other calls and the history write timed alone, and the CPU oracle on a
-    bounded sample.  Returns the result object (no driver-level keys)."""
+    bounded sample.  shared=True runs the decode through
+    pa_decode_attention_shared.  Returns the result object (no driver-level
+    keys)."""
+    import numpy as np
     import torch
 
     import paged_kv_cache_188_amd as pa
@@ -522,7 +532,7 @@ def decode_result(cid, args, cpu_seconds, separate=False):
     # work is then a few foreign-function calls, far less than its GPU time,
     # so the stream never runs dry between steps
     prepared = [dev.prepare(other_ops + decode_ops, k, stream=stream,
-                            vector_only=args.vector_only) for k in range(npools)]
+                            vector_only=args.vector_only, shared=shared) for k in range(npools)]
     n_other = len(other_ops)
     # When the step is the decode call(s) alone, one pair of HIP events spans
     # the K back-to-back steps; otherwise events bracket each step's decode
@@ -574,7 +584,16 @@ def decode_result(cid, args, cpu_seconds, separate=False):
                                         wl.partition_size, dev.torch_dtype,
                                         vector_only=args.vector_only)
     call = "pa_decode_attention_append" if appended else "pa_decode_attention"
-    if workers > 0:
+    if shared:
+        call = "pa_decode_attention_shared"
+        gs, sl, _ = dev.shared_args("final")
+        gs, sl = gs.cpu().numpy(), sl.cpu().numpy()
+        decomposition = {"path": "stream-K, shared prefixes", "persistent_waves": workers,
+                         "groups": int(len(sl)), "groups_sharing": int((sl > 0).sum()),
+                         "members_per_group": sorted(set(np.diff(gs).tolist()))}
+        kernel = (f"{call}: decode_mfma_streamk_kernel (prefix pass, own-token pass) + "
+                  "decode_streamk_merge_kernel x2 + decode_shared_combine_kernel")
+    elif workers > 0:
         decomposition = {"path": "stream-K", "persistent_waves": workers}
         kernel = f"{call}: decode_mfma_streamk_kernel + decode_streamk_merge_kernel"
     else:
@@ -598,14 +617,14 @@ def decode_result(cid, args, cpu_seconds, separate=False):
                              "decode call alone, divided by the step count"}
         kernel += f" (events around {args.steps} back-to-back calls)"
     kv_bytes = wl.kv_bytes_read()
-    dec_bytes = wl.decode_bytes()
+    dec_bytes = wl.shared_decode_bytes(gs, sl) if shared else wl.decode_bytes()
     if appended:  # the call also stores every non-empty sequence's new K/V row
         dec_bytes += int((wl.context_lens > 0).sum()) * wl.num_kv_heads * wl.head_dim * 2 \
             * (2 if wl.dtype == "bf16" else 4)
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     traffic, traffic_src = (None, None) if args.vector_only or args.partition is not None \
-        else measured_traffic(wl)
+        else measured_traffic(wl, call=call if shared else None)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -625,8 +644,7 @@ def decode_result(cid, args, cpu_seconds, separate=False):
             "max_context_len": wl.max_context_len,
             "decomposition": decomposition,
             "step_calls": [{"copy": "pa_copy_blocks", "write": "pa_write_kv_at",
-                            "decode": "pa_decode_attention",
-                            "decode_append": "pa_decode_attention_append"}[kind]
+                            "decode": call, "decode_append": call}[kind]
                            for kind, _ in ops],
             "seed": list(wl.seed), "pool_copies_rotated": npools,
             "parallelism": "single GPU",
@@ -652,7 +670,13 @@ def decode_result(cid, args, cpu_seconds, separate=False):
     res["other_ops"] = ops_timing
     res["history_write"] = hist
     uniq = wl.unique_kv_bytes()
-    if uniq < kv_bytes:
+    if shared:
+        res["roofline"]["note"] = (
+            "algorithmic bytes: each group's shared prefix read once, every sequence's own "
+            "tokens once, queries and outputs; value (logical bytes, every sequence's full "
+            "context, per step time) counts shared blocks once per sequence")
+        res["roofline"]["unique_kv_bytes"] = uniq
+    elif uniq < kv_bytes:
         # blocks shared between sequences: the call reads each sequence's
         # whole context through its table, and the repeated reads of shared
         # blocks can hit in the caches, so the logical-byte rate above is not
@@ -817,7 +841,8 @@ def main():
         study(args)
         return
     if args.config is not None:
-        res = decode_result(args.config, args, args.cpu_seconds, separate=args.separate)
+        res = decode_result(args.config, args, args.cpu_seconds, separate=args.separate,
+                            shared=args.shared)
         print(json.dumps(_driver_keys(res, args)), flush=True)
         return
     # default: the 70B-shaped batch is the headline; the 8B-shaped,
@@ -827,11 +852,12 @@ def main():
     print(f"[bench] {head['config']['workload']}: {head['roofline']['frac']}", file=sys.stderr,
           flush=True)
     subs = {}
-    for cid in (2, 4, 5):
-        r = decode_result(cid, args, args.sub_cpu_seconds, separate=args.separate)
-        subs[r["config"]["workload"]] = r
-        print(f"[bench] {r['config']['workload']}: {r['roofline']['frac']}", file=sys.stderr,
-              flush=True)
+    for cid, shared in ((2, False), (4, False), (4, True), (5, False)):
+        r = decode_result(cid, args, args.sub_cpu_seconds, separate=args.separate, shared=shared)
+        name = r["config"]["workload"] + (" | pa_decode_attention_shared" if shared else "")
+        subs[name] = r
+        print(f"[bench] {name}: {r['roofline']['frac']} {r['decode_call_us']['median']} us",
+              file=sys.stderr, flush=True)
     r = prefill_result(args, args.sub_cpu_seconds)
     subs[r["config"]["workload"]] = r
     print(f"[bench] {r['config']['workload']}: {r['roofline']['frac']}", file=sys.stderr,

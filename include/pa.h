@@ -13,6 +13,8 @@
  *   pa_decode_attention  one query token per sequence attends to its history,
  *                        reached block by block through its block table
  *   pa_decode_attention_append  the new tokens stored and attended in one call
+ *   pa_decode_attention_shared  the same for groups of sequences sharing a
+ *                        prefix, each shared block read once per group
  *   pa_prefill_attention  several query tokens per sequence (a prompt chunk),
  *                        causal, over the same pools
  *
@@ -342,6 +344,64 @@ pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache,
                                      int32_t partition_size, void* workspace,
                                      size_t workspace_bytes, pa_dtype dtype,
                                      uint32_t flags, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode_attention_shared  (decode of groups that share a prefix)
+ *
+ * [nalar] "Sharing blok dapat menghindari duplikasi state KV" and [gininih]
+ * "Cara kerja PagedAttention": sequences sampled from one prompt (parallel
+ * sampling, beam candidates) map the blocks of their common prefix to the
+ * same physical blocks.  This call computes exactly what
+ * pa_decode_attention_append (k_new / v_new given) or pa_decode_attention
+ * (both NULL) computes for the same arguments, but reads each shared block
+ * once per group instead of once per member: the pages' kernel reads every
+ * sequence's context through its own table, so a block shared by m
+ * sequences crosses the memory bus m times.
+ *
+ * Groups are consecutive ranges of sequences: group g holds sequences
+ * group_start[g] .. group_start[g+1]-1 (int32 [num_groups+1], increasing,
+ * group_start[0] = 0, group_start[num_groups] = num_seqs) whose first
+ * shared_len[g] tokens (int32 [num_groups]) map, block by block, to the same
+ * physical blocks in every member's table.  The library reads those tokens
+ * through the table of the group's first member.  Per group it uses the
+ * largest multiple of max(16, block_size) tokens that is <= shared_len[g]
+ * and < every member's context length (so each member's last token, the
+ * one a step appends, is always its own); only the first 16 / G members
+ * (G = num_q_heads / num_kv_heads) of a group are read together, later ones
+ * attend over their whole context on their own.  A group with a single
+ * member, or nothing left to share, is plain decode.  Both arrays live in
+ * device memory and are not validated on the host: a group layout that
+ * breaks this contract gives unspecified results, never an access outside
+ * a buffer.
+ *
+ * Two stream-K passes run: one over the (group, KV head) prefixes, the G
+ * heads of up to 16 / G members stacked in one matrix-core tile, then one
+ * over every (sequence, KV head)'s own tokens; a last kernel combines the
+ * two float32 results of each head with their log2-sum-exp (exact in real
+ * arithmetic; the rounding differs from the single-pass call within the
+ * decode tolerance).  bf16 K/V only, num_seqs <= 4096, 1 <= num_groups <=
+ * 2048, block_size >= 8; the workspace must hold
+ * pa_decode_shared_workspace_size() bytes, 256-byte aligned.  Other
+ * arguments, errors and determinism as pa_decode_attention_append.
+ * ------------------------------------------------------------------------- */
+size_t pa_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       pa_dtype dtype);
+
+pa_status pa_decode_attention_shared(float* out, const void* q, void* k_cache,
+                                     void* v_cache, const void* k_new,
+                                     const void* v_new, int64_t new_token_stride,
+                                     const int32_t* block_tables,
+                                     const int32_t* context_lens,
+                                     const int32_t* group_start,
+                                     const int32_t* shared_len, int32_t num_groups,
+                                     int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq,
+                                     int32_t max_context_len, float scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     pa_dtype dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * pa_decode_attention_noalloc  (decode with no allocation and no workspace)

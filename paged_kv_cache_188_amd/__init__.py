@@ -88,6 +88,11 @@ SIGNATURES = {
                                                    _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                    ctypes.c_float, _I32, ctypes.c_int,
                                                    ctypes.c_uint32, _P]),
+    "pa_decode_shared_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, ctypes.c_int]),
+    "pa_decode_attention_shared": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P,
+                                                  _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                  _I32, ctypes.c_float, _P, ctypes.c_size_t,
+                                                  ctypes.c_int, _P]),
     "pa_prefill_attention": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                             _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
                                             ctypes.c_int, _P]),
@@ -452,6 +457,115 @@ def decode_attention_noalloc(q, k_cache, v_cache, block_tables, context_lens, sc
         float(scale), int(partition_size), _dtype_code(k_cache),
         PA_DECODE_VECTOR_ONLY if vector_only else 0, _stream(stream)))
     return out
+
+
+def shared_prefix_groups(block_tables, context_lens, block_size, group):
+    """Host-side grouping for decode_attention_shared: (group_start,
+    shared_len) as int32 numpy arrays, from host copies of the block tables
+    [S][MB] and context lengths [S].
+
+    Consecutive sequences are grouped while they share leading physical
+    blocks with the group's first member, at most 16 // group of them (the
+    sequences whose query heads fill one matrix-core tile; group = query
+    heads per KV head), and only while a new member does not lower the
+    group's saving, (members - 1) x shared blocks.  shared_len is the shared
+    block count times block_size (0 for a lone sequence); the library trims
+    it further."""
+    import numpy as np
+    bt = np.asarray(block_tables)
+    ctx = np.asarray(context_lens).astype(np.int64)
+    S = ctx.shape[0]
+    cap = max(1, 16 // int(group))
+
+    def used(i):
+        n = int(-(-max(int(ctx[i]), 0) // block_size))
+        return bt[i, :min(n, bt.shape[1])]
+
+    def common(a, b):
+        m = min(a.shape[0], b.shape[0])
+        neq = np.nonzero((a[:m] != b[:m]) | (a[:m] < 0))[0]
+        return int(neq[0]) if neq.size else m
+
+    starts, lens = [0], []
+    i = 0
+    while i < S:
+        first = used(i)
+        members, blocks = 1, 0
+        while i + members < S and members < cap:
+            c = common(first, used(i + members))
+            new = c if members == 1 else min(blocks, c)
+            if new == 0 or members * new < (members - 1) * blocks:
+                break
+            blocks = new
+            members += 1
+        i += members
+        starts.append(i)
+        lens.append(blocks * block_size if members > 1 else 0)
+    return np.asarray(starts, dtype=np.int32), np.asarray(lens, dtype=np.int32)
+
+
+def decode_shared_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype=None):
+    """Workspace bytes for decode_attention_shared (bf16 only; 0 = unsupported)."""
+    import torch
+    code = PA_F32 if dtype == torch.float32 else PA_BF16
+    return int(lib().pa_decode_shared_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                     head_dim, code))
+
+
+def decode_attention_shared(q, k_cache, v_cache, block_tables, context_lens, group_start,
+                            shared_len, scale, max_context_len, workspace=None, out=None,
+                            stream=None, k_new=None, v_new=None, prepare=False):
+    """decode_attention (or its append form, with k_new / v_new) for groups
+    of consecutive sequences whose first shared_len[g] tokens map to the same
+    physical blocks (group g = sequences group_start[g] .. group_start[g+1]-1;
+    int32 device tensors of G+1 and G entries): each shared block is read
+    once per group (pa_decode_attention_shared)."""
+    import torch
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [S][Hq][D] and block_tables [S][MB]")
+    s, hq, d = q.shape
+    mb = block_tables.shape[1]
+    _shape(block_tables, (s, mb), "block_tables")
+    _shape(context_lens, (s,), "context_lens")
+    _shape(out, (s, hq, d), "out")
+    if group_start.dim() != 1 or group_start.numel() < 2:
+        raise ValueError("group_start must be [num_groups + 1]")
+    ng = group_start.numel() - 1
+    _shape(shared_len, (ng,), "shared_len")
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
+    if d2 != d:
+        raise ValueError("q and the pools disagree in head_dim")
+    _need(q, k_cache.dtype, "q")
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                    (group_start, "group_start"), (shared_len, "shared_len")):
+        _need(t, torch.int32, name)
+    need = decode_shared_workspace_size(s, hq, hkv, d, k_cache.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    if (k_new is None) != (v_new is None):
+        raise TypeError("give both k_new and v_new, or neither")
+    stride = 0
+    if k_new is not None:
+        if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+            raise TypeError("k_new and v_new must have the pool's element type")
+        if k_new.shape != (s, hkv, d) or v_new.shape != k_new.shape:
+            raise ValueError("k_new/v_new must be [S][Hkv][D]")
+        if k_new.stride(2) != 1 or k_new.stride(1) != d or v_new.stride() != k_new.stride():
+            raise ValueError("k_new/v_new rows must be contiguous [Hkv][D] with one token stride")
+        stride = k_new.stride(0)
+    args = (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), stride,
+            _ptr(block_tables), _ptr(context_lens), _ptr(group_start), _ptr(shared_len), ng, s,
+            hq, hkv, d, bs, nb, mb, int(max_context_len), float(scale),
+            _ptr(workspace) if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, _dtype_code(k_cache),
+            _stream(stream))
+    keep = (q, k_cache, v_cache, block_tables, context_lens, group_start, shared_len, workspace,
+            out, k_new, v_new)
+    call = PreparedCall("pa_decode_attention_shared", args, keep, out)
+    return call if prepare else call()
 
 
 def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,

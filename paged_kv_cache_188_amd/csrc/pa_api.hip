@@ -307,7 +307,9 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                       int32_t max_context_len, float scale, int32_t partition_size,
                       void* workspace, size_t workspace_bytes, pa_dtype dtype, uint32_t flags,
-                      bool append, bool static_scratch, void* stream) {
+                      bool append, bool static_scratch, void* stream,
+                      const int32_t* group_start = nullptr, const int32_t* shared_len = nullptr,
+                      int32_t num_groups = 0) {
   if (!valid_dtype(dtype)) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1 || max_context_len < 0 || num_q_heads % num_kv_heads)
@@ -335,9 +337,16 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
   if (path != pa::DecodePath::kStreamK && ((int64_t)num_seqs * num_kv_heads * P * 64 > UINT32_MAX ||
                                            (int64_t)num_seqs * num_q_heads * 256 > UINT32_MAX))
     return PA_ERR_SHAPE;
+  const bool shared = group_start != nullptr;
+  if (shared) {  // the two stream-K passes only
+    if (path != pa::DecodePath::kStreamK) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > pa::kSharedMaxSeqs || num_groups < 1 || num_groups > pa::kSharedMaxGroups)
+      return PA_ERR_SHAPE;
+  }
   if (num_seqs == 0) return PA_OK;
   const pa::DecodeWorkspace ws =
-      path == pa::DecodePath::kStreamK
+      shared ? pa::decode_workspace_shared(num_seqs, num_q_heads, head_dim)
+      : path == pa::DecodePath::kStreamK
           ? pa::decode_workspace_streamk(num_seqs, num_q_heads / num_kv_heads, head_dim)
           : pa::decode_workspace_partition(num_seqs, num_q_heads, head_dim, (int)P);
   if (static_scratch) {
@@ -347,6 +356,7 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
     if (ws.total > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PA_ERR_WORKSPACE;
   }
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (shared && !shared_len) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_UNSUPPORTED;
   const int e = elem_bytes(dtype);
@@ -377,6 +387,15 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
     p.ws_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
     if (path == pa::DecodePath::kStreamK)
       p.ws_handoff = reinterpret_cast<int32_t*>(wsb + ws.handoff_off);
+    if (shared) {
+      p.prefix_out = reinterpret_cast<float*>(wsb + ws.prefix_out_off);
+      p.prefix_lse = reinterpret_cast<float*>(wsb + ws.prefix_lse_off);
+      p.lse_out = reinterpret_cast<float*>(wsb + ws.lse_off);
+      p.group_start = group_start;
+      p.shared_len = shared_len;
+      p.num_groups = num_groups;
+      p.group_cap = 16 / (num_q_heads / num_kv_heads);
+    }
   }
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
@@ -443,6 +462,34 @@ pa_status pa_decode_attention_append(float* out, const void* q, void* k_cache, v
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
                      workspace, workspace_bytes, dtype, flags, true, false, stream);
+}
+
+size_t pa_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype) {
+  if (num_seqs <= 0 || num_seqs > pa::kSharedMaxSeqs || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > 16 ||
+      !supported_head_dim(head_dim) || dtype != PA_BF16)
+    return 0;
+  return pa::decode_workspace_shared(num_seqs, num_q_heads, head_dim).total;
+}
+
+pa_status pa_decode_attention_shared(float* out, const void* q, void* k_cache, void* v_cache,
+                                     const void* k_new, const void* v_new,
+                                     int64_t new_token_stride, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* group_start,
+                                     const int32_t* shared_len, int32_t num_groups,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, void* workspace, size_t workspace_bytes,
+                                     pa_dtype dtype, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PA_ERR_NULL;
+  if (!group_start) return PA_ERR_NULL;
+  return decode_impl(out, q, k_cache, v_cache, k_new, v_new, new_token_stride, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, scale, 0, workspace,
+                     workspace_bytes, dtype, 0, k_new != nullptr, false, stream, group_start,
+                     shared_len, num_groups);
 }
 
 pa_status pa_decode_attention_noalloc(float* out, const void* q, void* k_cache, void* v_cache,

@@ -132,11 +132,15 @@ struct MfmaState {
 // (zero rows for col >= G).
 template <int D>
 __device__ __forceinline__ void mfma_load_q(const DecodeParams& p, int seq, int hq0, int lane,
-                                            bf16x8_t (&qv)[D / 32]) {
+                                            bf16x8_t (&qv)[D / 32], int heads = 0) {
+  // heads > G: a shared-prefix group, tile column col is head hq0 + col % G
+  // of the group's member col / G (sequences seq, seq + 1, ...)
   const int grp = lane >> 4, col = lane & 15;
-  const bool valid = col < p.group;
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)seq * p.num_q_heads + hq0 + (valid ? col : 0)) * D;
+  const int G = p.group;
+  const bool valid = col < (heads > 0 ? heads : G);
+  const int64_t qr = valid ? (int64_t)(seq + col / G) * p.num_q_heads + hq0 + col % G
+                           : (int64_t)seq * p.num_q_heads + hq0;
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
     uint4 raw = make_uint4(0, 0, 0, 0);
@@ -358,13 +362,17 @@ __device__ __forceinline__ void mfma_tiles(const DecodeParams& p, int seq, int k
   }
 }
 
-// Write the G heads of a finished state: normalised into `out_row0` (head h
-// at out_row0 + h*D), or as a partial: acc at acc_row0 + h*acc_stride, m and
-// l at m0/l0 + h*ml_stride.
+// Write the `heads` heads of a finished state: normalised into `out_row0`,
+// head h at row (h / per) * member_rows + h % per (per = heads of one
+// sequence, member_rows = rows between the sequences of a shared-prefix
+// group; one sequence: row h), with its log2-sum-exp m + log2(l) at the same
+// row of lse_row0 when that is given; or as a partial: acc at acc_row0 +
+// h*acc_stride, m and l at m0/l0 + h*ml_stride.
 template <int D>
-__device__ __forceinline__ void mfma_finish(MfmaState<D>& st, int G, int lane, float* out_row0,
-                                            float* acc_row0, float* m0, float* l0,
-                                            int64_t acc_stride, int64_t ml_stride) {
+__device__ __forceinline__ void mfma_finish(MfmaState<D>& st, int heads, int per,
+                                            int64_t member_rows, int lane, float* out_row0,
+                                            float* lse_row0, float* acc_row0, float* m0,
+                                            float* l0, int64_t acc_stride, int64_t ml_stride) {
   constexpr int DV = D / 16;
   const int grp = lane >> 4, col = lane & 15;
   // total running sum per head (lanes of one column hold the same head)
@@ -376,10 +384,12 @@ __device__ __forceinline__ void mfma_finish(MfmaState<D>& st, int G, int lane, f
     const int h = 4 * grp + r;
     const float l_h = __shfl(l_run, h);
     const float m_h = __shfl(st.m_run, h);
-    if (h >= G) continue;
+    if (h >= heads) continue;
     if (out_row0) {
       const float inv = l_h > 0.f ? 1.0f / l_h : 0.f;
-      float* dst = out_row0 + (int64_t)h * D + DV * col;
+      const int64_t orow = (int64_t)(h / per) * member_rows + h % per;
+      if (lse_row0 && col == 0) lse_row0[orow] = l_h > 0.f ? m_h + __log2f(l_h) : kNegInf;
+      float* dst = out_row0 + orow * D + DV * col;
 #pragma unroll
       for (int c = 0; c < DV; c += 4)
         store_stream(dst + c, make_float4(st.acc[c][r] * inv, st.acc[c + 1][r] * inv,
@@ -402,19 +412,80 @@ __device__ __forceinline__ void mfma_finish(MfmaState<D>& st, int G, int lane, f
 // stream-K matrix-core kernel
 // ---------------------------------------------------------------------------
 
-// Exclusive prefix over sequences of their tile counts, into LDS (S+1
-// entries), computed by the whole workgroup.
-__device__ void tile_prefix(const DecodeParams& p, int* s_prefix) {
+// Passes of the stream-K kernels.  kPlain: every (sequence, KV head) over its
+// whole context.  The shared-prefix decode runs two passes: kPrefix, one
+// segment per (group, KV head) over the tokens the group's sequences share,
+// the G heads of each member stacked into one matrix-core tile of up to 16
+// heads, so each shared K/V tile is read once for the whole group; then
+// kOwn, every (sequence, KV head) over its own tokens after the shared ones;
+// a last kernel combines the two results of each head (log-sum-exp).
+enum : int { kPlain = 0, kPrefix = 1, kOwn = 2 };
+
+// Group g as the kernels see it: its first sequence, the members whose
+// prefix is shared (at most group_cap = 16 / G of them: the heads of one
+// tile), and the shared token count -- the caller's shared_len rounded down
+// to whole 16-token tiles and blocks, and cut so that every member keeps at
+// least its last token (the one a step appends) as its own.  count = 0: the
+// group shares nothing (or has a single member).  Every index is checked, so groups that break the
+// contract give wrong results, never an access outside a buffer.
+struct GroupInfo {
+  int first, count, len;
+};
+
+__device__ __forceinline__ GroupInfo group_info(const DecodeParams& p, int g) {
+  GroupInfo gi{0, 0, 0};
+  const int a = p.group_start[g], b = p.group_start[g + 1];
+  if (a < 0 || b <= a || a >= p.num_seqs) return gi;
+  const int cnt = min(min(b, p.num_seqs) - a, p.group_cap);
+  if (cnt < 2) return gi;  // a lone sequence: plain decode
+  const int unit = max(16, p.block_size);
+  int len = p.shared_len[g];
+  for (int i = 0; i < cnt; ++i) len = min(len, clamp_ctx(p, a + i) - 1);
+  len = len > 0 ? len - len % unit : 0;
+  if (len > 0) {
+    gi.first = a;
+    gi.count = cnt;
+    gi.len = len;
+  }
+  return gi;
+}
+
+// Exclusive prefix of the pass's tile counts per (virtual) sequence into LDS
+// (V + 1 entries; V = S, or the group count for kPrefix), computed by the
+// whole workgroup.  s_aux: kPrefix, the groups' first member, member count
+// and shared length ([3][V]); kOwn, each sequence's first own position ([S]).
+template <int MODE>
+__device__ void tile_prefix(const DecodeParams& p, int* s_prefix, int* s_aux) {
   __shared__ int wave_sums[kDecodeWaves];
   __shared__ int carry_s;
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
+  const int V = MODE == kPrefix ? p.num_groups : p.num_seqs;
+  if constexpr (MODE == kPrefix) {
+    for (int g = tid; g < V; g += blockDim.x) {
+      const GroupInfo gi = group_info(p, g);
+      s_aux[g] = gi.first;
+      s_aux[V + g] = gi.count;
+      s_aux[2 * V + g] = gi.len;
+    }
+  } else if constexpr (MODE == kOwn) {
+    for (int i = tid; i < V; i += blockDim.x) s_aux[i] = 0;
+    __syncthreads();
+    for (int g = tid; g < p.num_groups; g += blockDim.x) {
+      const GroupInfo gi = group_info(p, g);
+      for (int i = 0; i < gi.count; ++i) s_aux[gi.first + i] = gi.len;
+    }
+  }
   if (tid == 0) carry_s = 0;
   __syncthreads();
-  for (int base = 0; base < p.num_seqs; base += kDecodeWaves * kWave) {
+  for (int base = 0; base < V; base += kDecodeWaves * kWave) {
     const int i = base + tid;
     int v = 0;
-    if (i < p.num_seqs) v = (clamp_ctx(p, i) + 15) / 16;
+    if (i < V) {
+      if constexpr (MODE == kPrefix) v = s_aux[2 * V + i] / 16;
+      else if constexpr (MODE == kOwn) v = (clamp_ctx(p, i) - s_aux[i] + 15) / 16;
+      else v = (clamp_ctx(p, i) + 15) / 16;
+    }
     // inclusive scan within the wave
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -425,7 +496,7 @@ __device__ void tile_prefix(const DecodeParams& p, int* s_prefix) {
     __syncthreads();
     int before = carry_s;
     for (int w = 0; w < wave; ++w) before += wave_sums[w];
-    if (i < p.num_seqs) s_prefix[i + 1] = before + v;
+    if (i < V) s_prefix[i + 1] = before + v;
     __syncthreads();
     if (tid == 0) {
       int tot = 0;
@@ -487,39 +558,67 @@ __device__ __forceinline__ bool n_raw_ok(const TileDescs& d, int l, const Decode
   return n >= 1 && n <= p.max_tokens;
 }
 
-template <int BS>
+// First position of (virtual) sequence v's tiles in the pass, and the table
+// its tiles are read through (kPrefix: the group's first member's).
+template <int MODE>
+__device__ __forceinline__ int pass_pos0(const int* s_aux, int v) {
+  if constexpr (MODE == kOwn) return s_aux[v];
+  return 0;
+}
+template <int MODE>
+__device__ __forceinline__ int pass_table_seq(const int* s_aux, int v) {
+  if constexpr (MODE == kPrefix) return s_aux[v];
+  return v;
+}
+
+template <int BS, int MODE>
 __device__ __forceinline__ TileDescs describe_tiles(const DecodeParams& p, const int* s_prefix,
-                                                    Pos start, int count, int lane) {
+                                                    const int* s_aux, int V, Pos start, int count,
+                                                    int lane) {
   TileDescs d{0, 0, 0, 0, 0, 0};
   if (lane < count) {
-    const Pos q = advance(start, lane, s_prefix, p.num_seqs, p.num_kv_heads);
+    const Pos q = advance(start, lane, s_prefix, V, p.num_kv_heads);
     d.seq = q.seq;
     d.kvh = q.kvh;
     d.t = q.t;
-    d.n_raw = p.context_lens[q.seq];
-    const int32_t* row = p.block_tables + (int64_t)q.seq * p.max_blocks_per_seq;
-    d.phys_raw = row[(16 * q.t) / BS];
+    // the pass's context end: the shared length for a group, else the
+    // sequence's raw context length (checked when used)
+    d.n_raw = MODE == kPrefix ? s_aux[2 * V + q.seq] : p.context_lens[q.seq];
+    const int32_t* row =
+        p.block_tables + (int64_t)pass_table_seq<MODE>(s_aux, q.seq) * p.max_blocks_per_seq;
+    const int tpos = pass_pos0<MODE>(s_aux, q.seq) + 16 * q.t;
+    d.phys_raw = row[tpos / BS];
     if constexpr (BS < 16)  // the second block, when the table has one
-      d.phys_raw2 = (16 * q.t) / BS + 1 < p.max_blocks_per_seq ? row[(16 * q.t) / BS + 1] : -1;
+      d.phys_raw2 = tpos / BS + 1 < p.max_blocks_per_seq ? row[tpos / BS + 1] : -1;
   }
   return d;
 }
 
-template <int D, int BS>
+template <int D, int BS, int MODE>
 __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_kernel(
     const DecodeParams p) {
   static_assert(BS >= 16 || BS == 8, "a tile lies in one block, or covers two of 8");
-  extern __shared__ int s_prefix[];  // [S+1]
-  tile_prefix(p, s_prefix);
-  const int S = p.num_seqs;
+  // LDS: the tile prefix [V+1], then the pass's per-sequence data (tile_prefix)
+  extern __shared__ int s_lds[];
+  const int S = MODE == kPrefix ? p.num_groups : p.num_seqs;  // the pass's (virtual) sequences
+  int* s_prefix = s_lds;
+  int* s_aux = s_lds + S + 1;
+  tile_prefix<MODE>(p, s_prefix, s_aux);
   const int Hkv = p.num_kv_heads;
   const int G = p.group;
-  // sequences with an empty context: zeros, spread over the workgroups
-  for (int seq = blockIdx.x; seq < S; seq += gridDim.x) {
-    if (s_prefix[seq + 1] != s_prefix[seq]) continue;
-    float4* o = reinterpret_cast<float4*>(p.out + (int64_t)seq * p.num_q_heads * D);
-    for (int i = threadIdx.x; i < p.num_q_heads * (D / 4); i += blockDim.x)
-      o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // sequences with nothing to attend in the pass: zeros (and a log-sum-exp
+  // of -inf), spread over the workgroups; a group with no shared tokens
+  // writes nothing (its members' prefix results are not used)
+  if constexpr (MODE != kPrefix) {
+    for (int seq = blockIdx.x; seq < S; seq += gridDim.x) {
+      if (s_prefix[seq + 1] != s_prefix[seq]) continue;
+      float4* o = reinterpret_cast<float4*>(p.out + (int64_t)seq * p.num_q_heads * D);
+      for (int i = threadIdx.x; i < p.num_q_heads * (D / 4); i += blockDim.x)
+        o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (MODE == kOwn)
+        for (int i = threadIdx.x; i < p.num_q_heads; i += blockDim.x)
+          p.lse_out[(int64_t)seq * p.num_q_heads + i] = kNegInf;
+    }
   }
   const int64_t T = (int64_t)Hkv * s_prefix[S];
   const int64_t W = streamk_workers(T, p.max_workers);
@@ -551,12 +650,12 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
 
   // descriptors: `dc` covers the chunk the loads are in, `dn` the next one
   auto chunk_count = [&](int c) { return min(kWave, ntiles - c * kWave); };
-  TileDescs dc = describe_tiles<BS>(p, s_prefix, pos0, chunk_count(0), lane);
+  TileDescs dc = describe_tiles<BS, MODE>(p, s_prefix, s_aux, S, pos0, chunk_count(0), lane);
   dc.settle();
   Pos next_pos = advance(pos0, kWave, s_prefix, S, Hkv);
   TileDescs dn = {0, 0, 0, 0, 0, 0};
   if (ntiles > kWave) {
-    dn = describe_tiles<BS>(p, s_prefix, next_pos, chunk_count(1), lane);
+    dn = describe_tiles<BS, MODE>(p, s_prefix, s_aux, S, next_pos, chunk_count(1), lane);
     next_pos = advance(next_pos, kWave, s_prefix, S, Hkv);
   }
   int chunk = 0;
@@ -572,19 +671,28 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
   int2 my_handoff = make_int2(-1, -1);
   const int64_t slot0 = w * 2;
 
+  // heads per partial slot: a shared-prefix group stacks up to 16
+  const int HS = MODE == kPrefix ? 16 : G;
   auto finish_piece = [&]() {
     const int seq = cur_seg / Hkv, kvh = cur_seg - (cur_seg / Hkv) * Hkv;
     const int nt = s_prefix[seq + 1] - s_prefix[seq];
     const int hq0 = kvh * G;
     if (cur_t0 == 0 && cur_tlast == nt - 1) {
-      mfma_finish<D>(st, G, lane, p.out + ((int64_t)seq * p.num_q_heads + hq0) * D, nullptr,
-                     nullptr, nullptr, 0, 0);
+      if constexpr (MODE == kPrefix) {  // the group's members' prefix results
+        const int64_t r0 = (int64_t)s_aux[seq] * p.num_q_heads + hq0;
+        mfma_finish<D>(st, s_aux[S + seq] * G, G, p.num_q_heads, lane, p.prefix_out + r0 * D,
+                       p.prefix_lse + r0, nullptr, nullptr, nullptr, 0, 0);
+      } else {
+        const int64_t r0 = (int64_t)seq * p.num_q_heads + hq0;
+        mfma_finish<D>(st, G, G, 0, lane, p.out + r0 * D, MODE == kOwn ? p.lse_out + r0 : nullptr,
+                       nullptr, nullptr, nullptr, 0, 0);
+      }
     } else {
       // slot 0: a segment begun by an earlier wave; slot 1: one continued by
       // later waves -- this wave is its first, so it hands the merge on
       const int64_t slot = slot0 + (cur_t0 > 0 ? 0 : 1);
-      mfma_finish<D>(st, G, lane, nullptr, p.ws_acc + slot * G * D, p.ws_m + slot * G,
-                     p.ws_l + slot * G, D, 1);
+      mfma_finish<D>(st, MODE == kPrefix ? s_aux[S + seq] * G : G, G, 0, lane, nullptr, nullptr,
+                     p.ws_acc + slot * HS * D, p.ws_m + slot * HS, p.ws_l + slot * HS, D, 1);
       if (cur_t0 == 0) {
         const int64_t last_tile = (int64_t)Hkv * s_prefix[seq] + (int64_t)kvh * nt + nt - 1;
         my_handoff = make_int2(cur_seg, (int)(((last_tile + 1) * W - 1) / T));
@@ -605,7 +713,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
       dc = dn;
       dc.settle();
       if ((chunk + 1) * kWave < ntiles) {
-        dn = describe_tiles<BS>(p, s_prefix, next_pos, chunk_count(chunk + 1), lane);
+        dn = describe_tiles<BS, MODE>(p, s_prefix, s_aux, S, next_pos, chunk_count(chunk + 1),
+                                      lane);
         next_pos = advance(next_pos, kWave, s_prefix, S, Hkv);
       }
     }
@@ -620,17 +729,24 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
     const bool new_seg = seg != cur_seg;
     // A new segment's Q and the tile are loaded before the finished piece is
     // stored, so the waits on these loads need not cover those stores.
-    if (new_seg) mfma_load_q<D>(p, seq, kvh * G, lane, qv);
+    if (new_seg) {
+      if constexpr (MODE == kPrefix)
+        mfma_load_q<D>(p, s_aux[seq], kvh * G, lane, qv, s_aux[S + seq] * G);
+      else
+        mfma_load_q<D>(p, seq, kvh * G, lane, qv);
+    }
     const int64_t cb = ((int64_t)phys * Hkv + kvh) * ((int64_t)BS * D);
-    const int valid = min(16, n - 16 * t);
+    const int tpos = pass_pos0<MODE>(s_aux, seq) + 16 * t;  // the tile's first position
+    const int valid = min(16, n - tpos);
     // The tile holding the sequence's new token (position n-1) when the call
     // appends: that token is read from the new rows (the merge kernel stores
     // them into their slots, so no wave here waits for a store).
-    const bool append = p.k_new != nullptr && valid == n - 16 * t && n_raw_ok(dc, l, p);
+    const bool append = MODE != kPrefix && p.k_new != nullptr && valid == n - tpos &&
+                        n_raw_ok(dc, l, p);
     const int64_t row = (int64_t)seq * p.new_stride + (int64_t)kvh * D;
     Tile<D> b;
     if constexpr (BS >= 16) {
-      load_tile<D, BS>(kpool, vpool, cb, (16 * t) % BS, lane, b,
+      load_tile<D, BS>(kpool, vpool, cb, tpos % BS, lane, b,
                        static_cast<const uint16_t*>(p.k_new) + row,
                        static_cast<const uint16_t*>(p.v_new) + row, append ? valid - 1 : -1);
     } else {
@@ -658,10 +774,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
 // One workgroup per launched wave slot w.  If wave w handed a segment on, it
 // is merged here from slot 1 of wave w and slot 0 of waves w+1 .. last, in
 // wave order, with an online log-sum-exp rescale.
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeParams p) {
   constexpr int C = D / 4;  // float4 chunks per row
   const int G = p.group;
+  const int HS = MODE == kPrefix ? 16 : G;  // heads per partial slot
   if (blockIdx.x >= p.max_workers) {
     // Workgroups past the wave slots store the appended tokens: 8 (sequence,
     // KV head) rows per workgroup, 32 threads per row (16 K granules, 16 V
@@ -708,8 +825,20 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
   if (h.x < 0) return;
   const int seq = h.x / p.num_kv_heads, kvh = h.x % p.num_kv_heads;
   const int64_t w2 = h.y;
-  float* out = p.out + ((int64_t)seq * p.num_q_heads + kvh * G) * D;
-  for (int idx = threadIdx.x; idx < G * C; idx += blockDim.x) {
+  // where head hd of the segment goes: row0 + (hd / G) * member_rows + hd % G
+  int heads = G;
+  int64_t row0 = (int64_t)seq * p.num_q_heads + kvh * G, member_rows = 0;
+  float* out = p.out;
+  float* lse = MODE == kOwn ? p.lse_out : nullptr;
+  if constexpr (MODE == kPrefix) {  // a group: its members' prefix results
+    const GroupInfo gi = group_info(p, seq);
+    heads = gi.count * G;
+    row0 = (int64_t)gi.first * p.num_q_heads + kvh * G;
+    member_rows = p.num_q_heads;
+    out = p.prefix_out;
+    lse = p.prefix_lse;
+  }
+  for (int idx = threadIdx.x; idx < heads * C; idx += blockDim.x) {
     const int hd = idx / C, c = idx % C;
     float M = kNegInf, L = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -723,9 +852,9 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
       for (int u = 0; u < kBatch; ++u) {
         const int64_t w = wb + u <= w2 ? wb + u : w2;
         const int64_t slot = 2 * w + (w == w1 ? 1 : 0);
-        m[u] = p.ws_m[slot * G + hd];
-        l[u] = p.ws_l[slot * G + hd];
-        v[u] = reinterpret_cast<const float4*>(p.ws_acc + (slot * G + hd) * D)[c];
+        m[u] = p.ws_m[slot * HS + hd];
+        l[u] = p.ws_l[slot * HS + hd];
+        v[u] = reinterpret_cast<const float4*>(p.ws_acc + (slot * HS + hd) * D)[c];
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -742,8 +871,50 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
       }
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    store_stream(out + (int64_t)hd * D + 4 * c,
-                 make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv));
+    const int64_t orow = row0 + (int64_t)(hd / G) * member_rows + hd % G;
+    store_stream(out + orow * D + 4 * c, make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv));
+    if (lse && c == 0) lse[orow] = L > 0.f ? M + __log2f(L) : kNegInf;
+  }
+}
+
+// Shared-prefix decode, last step: for every member of a group that shares
+// a prefix, each head's prefix result (o_p, log2-sum-exp lp) and own-token
+// result (o_t, lt) are combined exactly:
+//     out = (2^lp o_p + 2^lt o_t) / (2^lp + 2^lt)
+// One workgroup per sequence; sequences outside a sharing group keep their
+// own-token result, which is then their whole context's.
+template <int D>
+__global__ __launch_bounds__(256) void decode_shared_combine_kernel(const DecodeParams p) {
+  constexpr int C = D / 4;
+  const int seq = blockIdx.x;
+  // the group holding seq: the last g with group_start[g] <= seq (bounded
+  // search; groups are consecutive ranges of sequences)
+  int lo = 0, hi = p.num_groups - 1, g = -1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) / 2;
+    if (p.group_start[mid] <= seq) {
+      g = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  if (g < 0) return;
+  const GroupInfo gi = group_info(p, g);
+  if (gi.count == 0 || seq < gi.first || seq >= gi.first + gi.count) return;
+  const int64_t r0 = (int64_t)seq * p.num_q_heads;
+  for (int idx = threadIdx.x; idx < p.num_q_heads * C; idx += blockDim.x) {
+    const int hd = idx / C, c = idx % C;
+    const float lp = p.prefix_lse[r0 + hd], lt = p.lse_out[r0 + hd];
+    const float M = fmaxf(lp, lt);
+    const float wp = M == kNegInf ? 0.f : fast_exp2(lp - M);
+    const float wt = M == kNegInf ? 0.f : fast_exp2(lt - M);
+    const float inv = wp + wt > 0.f ? 1.0f / (wp + wt) : 0.f;
+    const float4 op = reinterpret_cast<const float4*>(p.prefix_out + (r0 + hd) * D)[c];
+    float4* dst = reinterpret_cast<float4*>(p.out + (r0 + hd) * D) + c;
+    const float4 ot = *dst;
+    *dst = make_float4((wp * op.x + wt * ot.x) * inv, (wp * op.y + wt * ot.y) * inv,
+                       (wp * op.z + wt * ot.z) * inv, (wp * op.w + wt * ot.w) * inv);
   }
 }
 
@@ -786,11 +957,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_kernel(co
   mfma_tiles<D, BS>(p, it.seq, it.kvh, it.n, it.start / 16, (it.end + 15) / 16, qv, st, lane);
   const int64_t row = (int64_t)it.seq * p.num_q_heads + hq0;
   if (it.nparts <= 1) {
-    mfma_finish<D>(st, G, lane, p.out + row * D, nullptr, nullptr, nullptr, 0, 0);
+    mfma_finish<D>(st, G, G, 0, lane, p.out + row * D, nullptr, nullptr, nullptr, nullptr, 0, 0);
   } else {
     const int64_t prow = row * p.max_partitions + it.part;
-    mfma_finish<D>(st, G, lane, nullptr, p.ws_acc + prow * D, p.ws_m + prow, p.ws_l + prow,
-                   (int64_t)p.max_partitions * D, p.max_partitions);
+    mfma_finish<D>(st, G, G, 0, lane, nullptr, nullptr, p.ws_acc + prow * D, p.ws_m + prow,
+                   p.ws_l + prow, (int64_t)p.max_partitions * D, p.max_partitions);
   }
 }
 
@@ -1025,19 +1196,37 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(const Dec
 // launch helpers
 // ---------------------------------------------------------------------------
 
-template <int D, int BS>
-hipError_t launch_streamk(const DecodeParams& p, hipStream_t stream) {
+template <int D, int BS, int MODE>
+hipError_t launch_streamk_pass(const DecodeParams& p, hipStream_t stream) {
   const int blocks = p.max_workers / kDecodeWaves;
-  const size_t lds = (size_t)(p.num_seqs + 1) * sizeof(int);
-  hipLaunchKernelGGL((decode_mfma_streamk_kernel<D, BS>), dim3(blocks),
+  const int V = MODE == kPrefix ? p.num_groups : p.num_seqs;
+  const size_t lds =
+      (size_t)(V + 1 + (MODE == kPrefix ? 3 * V : MODE == kOwn ? V : 0)) * sizeof(int);
+  hipLaunchKernelGGL((decode_mfma_streamk_kernel<D, BS, MODE>), dim3(blocks),
                      dim3(kDecodeWaves * kWave), lds, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // merge workgroups (one per wave slot), then the append workgroups
   const int64_t append_rows = p.k_new ? (int64_t)p.num_seqs * p.num_kv_heads : 0;
   const int64_t grid = (int64_t)blocks * kDecodeWaves + (append_rows + 7) / 8;
-  hipLaunchKernelGGL((decode_streamk_merge_kernel<D>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     p);
+  hipLaunchKernelGGL((decode_streamk_merge_kernel<D, MODE>), dim3((unsigned)grid), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch_streamk(const DecodeParams& p, hipStream_t stream) {
+  if (!p.group_start) return launch_streamk_pass<D, BS, kPlain>(p, stream);
+  // shared prefixes: the groups' prefixes (nothing appended there: a group's
+  // shared tokens end before every member's last token), then every
+  // sequence's own tokens (with the new rows), then the combination
+  DecodeParams pp = p;
+  pp.k_new = pp.v_new = nullptr;
+  hipError_t e = launch_streamk_pass<D, BS, kPrefix>(pp, stream);
+  if (e != hipSuccess) return e;
+  e = launch_streamk_pass<D, BS, kOwn>(p, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_shared_combine_kernel<D>), dim3(p.num_seqs), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1091,9 +1280,11 @@ int streamk_workers_per_cu(int head_dim) {
   int blocks = 0;
   const size_t lds = (size_t)(kStreamKMaxSeqs + 1) * sizeof(int);
   hipError_t e = head_dim == 128
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma_streamk_kernel<128, 16>,
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks,
+                                                     decode_mfma_streamk_kernel<128, 16, kPlain>,
                                                      kDecodeWaves * kWave, lds)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_mfma_streamk_kernel<64, 16>,
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks,
+                                                     decode_mfma_streamk_kernel<64, 16, kPlain>,
                                                      kDecodeWaves * kWave, lds);
   if (e != hipSuccess || blocks <= 0) return -1;
   return blocks * kDecodeWaves;
@@ -1116,6 +1307,19 @@ DecodeWorkspace decode_workspace_partition(int num_seqs, int num_q_heads, int he
   w.l_off = align256(rows * sizeof(float));
   w.acc_off = w.l_off + align256(rows * sizeof(float));
   w.total = w.acc_off + align256(rows * head_dim * sizeof(float));
+  return w;
+}
+
+DecodeWorkspace decode_workspace_shared(int num_seqs, int num_q_heads, int head_dim) {
+  // stream-K partials with 16 heads per slot (the prefix pass's widest
+  // segments; the own-token pass reuses them), then the prefix results and
+  // the log2-sum-exp of both passes
+  DecodeWorkspace w = decode_workspace_streamk(num_seqs, 16, head_dim);
+  const size_t rows = (size_t)num_seqs * num_q_heads;
+  w.prefix_out_off = w.total;
+  w.prefix_lse_off = w.prefix_out_off + align256(rows * head_dim * sizeof(float));
+  w.lse_off = w.prefix_lse_off + align256(rows * sizeof(float));
+  w.total = w.lse_off + align256(rows * sizeof(float));
   return w;
 }
 

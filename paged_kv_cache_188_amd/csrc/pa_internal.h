@@ -78,6 +78,15 @@ struct DecodeParams {
                       // max_blocks_per_seq * block_size), so no index leaves its buffer
   int max_workers;    // stream-K path: waves launched (slot capacity of the workspace)
   float scale_log2;   // scale * log2(e)
+  // shared-prefix decode (else group_start is null): groups of consecutive
+  // sequences sharing the blocks of their first tokens
+  const int32_t* group_start;  // [num_groups + 1]
+  const int32_t* shared_len;   // [num_groups], tokens
+  int num_groups;
+  int group_cap;               // most members of a group whose prefix is shared: 16 / group
+  float* prefix_out;           // [S][Hq][D]: each member's attention over its group's prefix
+  float* prefix_lse;           // [S][Hq]: its log2-sum-exp
+  float* lse_out;              // [S][Hq]: log2-sum-exp of the own-token pass's `out`
 };
 
 // Stream-K decomposition limits.
@@ -107,10 +116,15 @@ hipError_t launch_prefill(const DecodeParams& p, const int32_t* query_start, int
 
 // Workspace offsets (bytes); shared by the size query and the launch.
 struct DecodeWorkspace {
-  size_t m_off, l_off, acc_off, handoff_off, total;
+  size_t m_off, l_off, acc_off, handoff_off, prefix_out_off, prefix_lse_off, lse_off, total;
 };
 DecodeWorkspace decode_workspace_partition(int num_seqs, int num_q_heads, int head_dim,
                                            int max_partitions);
 DecodeWorkspace decode_workspace_streamk(int num_seqs, int group, int head_dim);
+DecodeWorkspace decode_workspace_shared(int num_seqs, int num_q_heads, int head_dim);
+
+// Shared-prefix decode limits (LDS of the stream-K passes).
+constexpr int kSharedMaxSeqs = 4096;
+constexpr int kSharedMaxGroups = 2048;
 
 }  // namespace pa

@@ -365,3 +365,60 @@ def test_noalloc_limit_matches_header():
     text = open(os.path.join(ROOT, "include", "pa.h")).read()
     m = re.search(r"#define PA_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == pa.PA_NOALLOC_MAX_WORKSPACE
+
+
+def test_shared_decode_validation(lib):
+    """pa_decode_attention_shared: bf16 stream-K only, group and batch
+    limits, its own workspace size; all refused before any HIP call."""
+    need = lib.pa_decode_shared_workspace_size(2, 8, 2, 128, 1)
+    assert need > lib.pa_decode_workspace_size(2, 8, 2, 128, 16, 40, 0, 1, 0)
+    assert lib.pa_decode_shared_workspace_size(2, 8, 2, 128, 0) == 0       # f32
+    assert lib.pa_decode_shared_workspace_size(4097, 8, 2, 128, 1) == 0
+    assert lib.pa_decode_shared_workspace_size(2, 34, 2, 128, 1) == 0      # group of 17
+    sh = lambda **k: lib.pa_decode_attention_shared(
+        k.get("out", FAKE), FAKE, FAKE, FAKE, k.get("kn", FAKE), k.get("vn", FAKE), 0, FAKE,
+        FAKE, k.get("gs", FAKE), k.get("sl", FAKE), k.get("ng", 1), k.get("S", 2), 8, 2, 128,
+        k.get("bs", 16), 10, 4, 40, 0.1, k.get("ws", FAKE), k.get("ws_bytes", need),
+        k.get("dtype", 1), NULL)
+    assert sh(gs=NULL) == NUL
+    assert sh(sl=NULL) == NUL
+    assert sh(kn=NULL) == NUL                  # one of the new rows without the other
+    assert sh(out=NULL) == NUL
+    assert sh(dtype=0) == UNSUP                # f32: no matrix-core passes
+    assert sh(bs=4) == UNSUP
+    assert sh(ng=0) == SHAPE
+    assert sh(ng=2049) == SHAPE
+    assert sh(S=4097) == SHAPE
+    assert sh(ws_bytes=need - 1) == WS
+    assert sh(ws=NULL) == WS
+    assert sh(ws=ctypes.c_void_p(0x10010)) == WS
+    assert sh(S=0, out=NULL) == OK
+
+
+def test_shared_prefix_groups_host_logic():
+    import numpy as np
+    import workloads as W
+    # the shared-prefix workload: samples of one prompt share all but the
+    # copied-on-write last prefix block; G = 4 puts 4 of them in a tile
+    wl = W.make(4, small=True)
+    gs, sl = pa.shared_prefix_groups(wl.tables["final"], wl.context_lens, wl.block_size, 4)
+    npb = -(-wl.notes["prefix"] // wl.block_size)
+    assert gs.tolist() == list(range(0, wl.num_seqs + 1, 4))
+    assert sl.tolist() == [(npb - 1) * wl.block_size] * (wl.num_seqs // 4)
+    # G = 16: one sequence per tile, nothing is shared
+    gs, sl = pa.shared_prefix_groups(wl.tables["final"], wl.context_lens, wl.block_size, 16)
+    assert gs.tolist() == list(range(wl.num_seqs + 1)) and not sl.any()
+    # no common blocks: lone sequences
+    bt = np.arange(12, dtype=np.int32).reshape(3, 4)
+    gs, sl = pa.shared_prefix_groups(bt, np.array([64, 64, 64]), 16, 1)
+    assert gs.tolist() == [0, 1, 2, 3] and sl.tolist() == [0, 0, 0]
+    # a member that would cut the group's saving starts a new group
+    bt = np.array([[1, 2, 3, 4], [1, 2, 3, 5], [1, 9, 9, 9], [1, 9, 8, 8]], dtype=np.int32)
+    gs, sl = pa.shared_prefix_groups(bt, np.array([64, 64, 64, 64]), 16, 1)
+    assert gs.tolist() == [0, 2, 4] and sl.tolist() == [48, 32]
+    # entries past a context's last block and -1 entries are not shared
+    bt = np.array([[1, 2, -1, -1], [1, 2, -1, -1]], dtype=np.int32)
+    gs, sl = pa.shared_prefix_groups(bt, np.array([20, 40]), 16, 1)
+    assert sl.tolist() == [32]
+    gs, sl = pa.shared_prefix_groups(bt, np.array([20, 10]), 16, 1)
+    assert sl.tolist() == [16]

@@ -162,6 +162,25 @@ class Workload:
         t = int(self.query_start[-1])
         return (self.kv_bytes_read() + t * self.num_q_heads * self.head_dim * (e + 4))
 
+    def shared_decode_bytes(self, group_start, shared_len) -> int:
+        """decode_bytes() for a call that reads each group's shared tokens
+        once: group g's first min(members, 16 // G) sequences share the largest
+        multiple of max(16, block_size) tokens <= shared_len[g] and < each
+        one's context (the tokens the shared-prefix call reads once)."""
+        unit = max(16, self.block_size)
+        cap = 16 // self.group
+        per_token = self.num_kv_heads * self.head_dim * 2 * elem_bytes(self.dtype)
+        saved = 0
+        for g in range(len(shared_len)):
+            a, b = int(group_start[g]), int(group_start[g + 1])
+            cnt = min(b - a, cap)
+            if cnt < 2:
+                continue
+            n = min(int(shared_len[g]), int(self.context_lens[a:a + cnt].min()) - 1)
+            n = n - n % unit if n > 0 else 0
+            saved += (cnt - 1) * n * per_token
+        return self.decode_bytes() - saved
+
     def unique_kv_bytes(self) -> int:
         """KV bytes of distinct physical blocks referenced by the final tables."""
         bt = self.tables["final"]

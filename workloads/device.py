@@ -50,6 +50,7 @@ class DeviceWorkload:
         self.max_ctx = wl.max_context_len
         self.torch_dtype = torch.bfloat16 if wl.dtype == BF16 else torch.float32
         self.workspace = torch.empty(1, dtype=torch.uint8, device=device)
+        self._shared = {}
         self._ensure_workspace(wl.partition_size, False)
         self.setup_ops = [self._upload(op) for op in wl.setup]
         self.step_ops = [self._upload(op) for op in wl.step]
@@ -110,14 +111,48 @@ class DeviceWorkload:
             self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self.workspace
 
+    def shared_args(self, table):
+        """(group_start, shared_len, workspace) of pa_decode_attention_shared
+        for `table`: the groups pa.shared_prefix_groups finds in its host copy."""
+        if table not in self._shared:
+            wl = self.wl
+            gs, sl = pa.shared_prefix_groups(wl.tables[table], wl.context_lens, wl.block_size,
+                                             wl.group)
+            need = pa.decode_shared_workspace_size(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
+                                                   wl.head_dim, self.torch_dtype)
+            if not need:
+                raise ValueError(f"{wl.name}: no shared-prefix decode for these shapes")
+            self._shared[table] = (torch.from_numpy(gs).to(self.device),
+                                   torch.from_numpy(sl).to(self.device),
+                                   torch.empty(need, dtype=torch.uint8, device=self.device))
+        return self._shared[table]
+
+    def _decode_call(self, kind, x, k, v, part, vector_only, stream, shared, prepare):
+        """One decode (or decode_append) op: pa_decode_attention(_append), or
+        with shared=True pa_decode_attention_shared over the table's groups."""
+        wl = self.wl
+        table = x["table"] if kind == "decode_append" else x
+        kw = dict(k_new=x["k"], v_new=x["v"]) if kind == "decode_append" else {}
+        if shared:
+            gs, sl, ws = self.shared_args(table)
+            return pa.decode_attention_shared(self.q, k, v, self.tables[table], self.ctx, gs, sl,
+                                              wl.scale, self.max_ctx, workspace=ws, out=self.out,
+                                              stream=stream, prepare=prepare, **kw)
+        return pa.decode_attention(self.q, k, v, self.tables[table], self.ctx, wl.scale,
+                                   self.max_ctx, partition_size=part,
+                                   workspace=self._ensure_workspace(part, vector_only),
+                                   out=self.out, vector_only=vector_only, stream=stream,
+                                   prepare=prepare, **kw)
+
     # -------------------------------------------------------------------
     def _run(self, ops, pool=0, partition_size=None, vector_only=False, stream=None,
-             fused_write=True, record_slots=True):
+             fused_write=True, record_slots=True, shared=False):
         """Run `ops`.  A write is one pa_write_kv_at launch (slots computed and
         stored in the same kernel) or, with fused_write=False, pa_compute_slots
         followed by pa_write_kv.  A decode_append op is one
         pa_decode_attention_append call; with record_slots its write's slots
-        are also computed (pa_compute_slots) for checking."""
+        are also computed (pa_compute_slots) for checking.  shared=True runs
+        every decode through pa_decode_attention_shared."""
         wl = self.wl
         k, v = self.pools[pool]
         part = wl.partition_size if partition_size is None else partition_size
@@ -128,11 +163,7 @@ class DeviceWorkload:
                     pa.compute_slots(self.tables[x["table"]], w["positions"], wl.block_size,
                                      wl.num_blocks, seq_ids=w["seq_ids"], out=w["slots"],
                                      stream=stream)
-                ws = self._ensure_workspace(part, vector_only)
-                pa.decode_attention(self.q, k, v, self.tables[x["table"]], self.ctx, wl.scale,
-                                    self.max_ctx, partition_size=part, workspace=ws, out=self.out,
-                                    vector_only=vector_only, stream=stream, k_new=x["k"],
-                                    v_new=x["v"])
+                self._decode_call(kind, x, k, v, part, vector_only, stream, shared, False)
                 continue
             if kind == "write" and fused_write:
                 pa.write_kv_at(k, v, x["k"], x["v"], self.tables[x["table"]], x["positions"],
@@ -148,13 +179,11 @@ class DeviceWorkload:
                 pa.prefill_attention(self.q, k, v, self.tables[x], self.ctx, self.qs, wl.scale,
                                      wl.max_query_len, out=self.out, stream=stream)
             else:
-                ws = self._ensure_workspace(part, vector_only)
-                pa.decode_attention(self.q, k, v, self.tables[x], self.ctx, wl.scale, self.max_ctx,
-                                    partition_size=part, workspace=ws, out=self.out,
-                                    vector_only=vector_only, stream=stream)
+                self._decode_call(kind, x, k, v, part, vector_only, stream, shared, False)
         return self.out
 
-    def prepare(self, ops, pool=0, partition_size=None, stream=None, vector_only=False):
+    def prepare(self, ops, pool=0, partition_size=None, stream=None, vector_only=False,
+                shared=False):
         """Zero-argument callables that issue `ops` on pool copy `pool`, as
         _run does with record_slots=False; the decode calls are validated and
         marshalled here once (pa.PreparedCall), so issuing one costs a single
@@ -166,12 +195,8 @@ class DeviceWorkload:
         for op in ops:
             kind, x = op
             if kind in ("decode", "decode_append"):
-                table = x["table"] if kind == "decode_append" else x
-                kw = dict(k_new=x["k"], v_new=x["v"]) if kind == "decode_append" else {}
-                calls.append(pa.decode_attention(
-                    self.q, k, v, self.tables[table], self.ctx, wl.scale, self.max_ctx,
-                    partition_size=part, workspace=self._ensure_workspace(part, vector_only),
-                    out=self.out, stream=stream, prepare=True, vector_only=vector_only, **kw))
+                calls.append(self._decode_call(kind, x, k, v, part, vector_only, stream, shared,
+                                               True))
             elif kind == "write":
                 calls.append(pa.write_kv_at(k, v, x["k"], x["v"], self.tables[x["table"]],
                                             x["positions"], seq_ids=x["seq_ids"],
@@ -180,7 +205,8 @@ class DeviceWorkload:
                 calls.append(pa.copy_blocks(k, v, x, stream=stream, prepare=True))
             else:
                 calls.append(lambda op=op: self._run([op], pool, partition_size=part,
-                                                     stream=stream, record_slots=False))
+                                                     stream=stream, record_slots=False,
+                                                     shared=shared))
         return calls
 
     def run_setup(self, pool=0, **kw):
