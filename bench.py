@@ -281,6 +281,13 @@ def prefill_result(args, cpu_seconds):
             "algorithmic_flops_per_launch": flops, "avg_launch_us": round(att_avg * 1e3, 2),
         },
     }
+    traffic, src = measured_traffic(wl, "pa_prefill.hip")
+    if traffic:
+        res["roofline"]["traffic"] = traffic
+        res["roofline"]["traffic_source"] = src
+        res["roofline"]["traffic_note"] = (
+            "HBM bytes per call (K/V reads, mostly served from L2 after the first query tile, "
+            "and the float32 output); the bound is the matrix cores, not this traffic")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(wl, cpu_seconds)
     del prepared, dev
@@ -479,7 +486,10 @@ def other_ops_timing(torch, dev, wl, npools, stream, reps=20):
 def history_write_timing(torch, dev, wl, stream, reps=5):
     """The workload's history fill at scale: each setup write
     (pa_write_kv_at of every cached token) timed alone, one event pair around
-    reps back-to-back calls; bytes are the K/V rows read plus written."""
+    reps back-to-back calls; bytes are the K/V rows read plus written.  Beside
+    it, torch's device-to-device copy of a contiguous buffer of the rows' size
+    (the same bytes read and written, no scatter) as the box's read + write
+    reference."""
     e = 2 if wl.dtype == "bf16" else 4
     out = []
     for op in dev.setup_ops:
@@ -492,8 +502,18 @@ def history_write_timing(torch, dev, wl, stream, reps=5):
         t = int(x["positions"].numel())
         nbytes = 2 * 2 * t * wl.num_kv_heads * wl.head_dim * e + 20 * t
         gbps = nbytes / (ms * 1e-3) / 1e9
+        rows = 2 * t * wl.num_kv_heads * wl.head_dim * e
+        src = torch.empty(rows, dtype=torch.uint8, device=dev.device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        cms = _span_ms(torch, stream, lambda r: dst.copy_(src), reps)
+        cgbps = 2 * rows / (cms * 1e-3) / 1e9
+        del src, dst
         out.append({"call": "pa_write_kv_at", "tokens": t, "us": round(ms * 1e3, 1),
-                    "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+                    "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                    "torch_copy_same_bytes": {"us": round(cms * 1e3, 1), "gbps": round(cgbps, 1),
+                                              "frac_of_hbm_peak":
+                                                  round(cgbps / HBM_PEAK_GBPS, 4)}})
     return out
 
 
