@@ -30,13 +30,18 @@
 //                 running max moved only when a score passes it by 8 (as in
 //                 the decode); each row hides keys past its own position
 //                 (causal), which only steps on the diagonal need to check;
-//   O += P V      v_mfma_f32_16x16x32_bf16 with A = P (16 rows x 32 keys,
+//   O += P V      v_mfma_f32_16x16x32_f16 with A = P (16 rows x 32 keys,
 //                 taken straight from the scores' registers: k index
 //                 8*grp + e is key 4*grp + e of half 0 for e < 4 and of half
-//                 1 for e >= 4) and B = V in the same key order.  P is split
-//                 into hi + lo bf16 parts (hi = upper 16 bits, lo = the
-//                 rounded rest), so the weights keep float32 accuracy;
-//                 bf16 x bf16 products are exact and accumulate in float32.
+//                 1 for e >= 4) and B = V in the same key order, both fp16:
+//                 the weights (in [0, 256] under the lazy maximum) keep 11
+//                 significant bits, and V, scaled by 2^-4 when it is staged
+//                 in LDS, is exact in fp16 for 2^-10 <= |v| <= 1.05e6; the
+//                 products accumulate in float32.  (bf16 weights would keep
+//                 8 bits: on the chunked-prefill workload that puts the
+//                 maximum error at 2.8e-3 against the oracle, over the
+//                 2e-3 bound; fp16 gives 4.0e-4, and needs one MFMA per tile
+//                 where the hi + lo bf16 split of the weights needed two.)
 //                 V's B operand (keys along k) is read from the row-major
 //                 V tile with gfx950's transposing LDS load
 //                 (ds_read_b64_tr_b16); one 16-byte pad per V row spreads
@@ -78,6 +83,8 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -103,27 +110,32 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ f16x8_t as_f16x8(u32x4_t v) { return __builtin_bit_cast(f16x8_t, v); }
 
-// hi + lo bf16 split of 8 float32 weights, packed as two A operands
-__device__ __forceinline__ void split_weights(const float (&p)[8], bf16x8_t& hi, bf16x8_t& lo) {
-  uint32_t u[8];
-  float r[8];
+// Two float32 values as a packed fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+
+// Eight float32 weights as an fp16 A operand.
+__device__ __forceinline__ f16x8_t weights_f16(const float (&p)[8]) {
+  return as_f16x8(u32x4_t{pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]),
+                          pack_f16(p[6], p[7])});
+}
+
+// A 16-byte chunk of 8 bf16 V values as 8 fp16 values of V * 2^-4 (an
+// exact scaling; the output is scaled back by 2^4).  Values up to
+// 65504 * 2^4 (1.05e6) in magnitude keep 11 significant bits (more than
+// bf16's 8); below 2^-10 they become fp16 subnormals, with an absolute error
+// under 2^-21.
+constexpr float kVScale = 1.0f / 16.0f;
+__device__ __forceinline__ u32x4_t v_to_f16(u32x4_t v) {
+  u32x4_t r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    u[i] = __float_as_uint(p[i]);
-    r[i] = p[i] - __uint_as_float(u[i] & 0xffff0000u);  // exact
-  }
-  u32x4_t h, l;
-  h.x = __builtin_amdgcn_perm(u[1], u[0], 0x07060302u);
-  h.y = __builtin_amdgcn_perm(u[3], u[2], 0x07060302u);
-  h.z = __builtin_amdgcn_perm(u[5], u[4], 0x07060302u);
-  h.w = __builtin_amdgcn_perm(u[7], u[6], 0x07060302u);
-  l.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[0], r[1]}, bf16x2_t));
-  l.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[2], r[3]}, bf16x2_t));
-  l.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[4], r[5]}, bf16x2_t));
-  l.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r[6], r[7]}, bf16x2_t));
-  hi = as_bf16x8(h);
-  lo = as_bf16x8(l);
+  for (int i = 0; i < 4; ++i)
+    r[i] = pack_f16(__uint_as_float(v[i] << 16) * kVScale,
+                    __uint_as_float(v[i] & 0xffff0000u) * kVScale);
+  return r;
 }
 
 // Global -> register loads of one 16-key half for thread u (0..127) of the
@@ -265,6 +277,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
   constexpr int CH = D / 64;   // chunks per thread per half, K and V each
   constexpr int VRS = GR + 1;   // V row stride in 16-byte units: one unit of padding
   // [buffer][K: half, granule, key | V: key, granule (+ pad)] in 16-byte units
+  // [buffer][K (bf16): half, granule, key | V (fp16, scaled): key, granule (+ pad)]
   __shared__ u32x4_t smem[2][2 * HALF + kStep * VRS];
 
   const int tid = threadIdx.x;
@@ -382,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
     for (int i = 0; i < CH; ++i) {
       const int c = u + 128 * i;
       buf[th * HALF + c] = kreg[i];
-      buf[2 * HALF + (th * 16 + c / GR) * VRS + c % GR] = vreg[i];
+      buf[2 * HALF + (th * 16 + c / GR) * VRS + c % GR] = v_to_f16(vreg[i]);
     }
     lds_barrier();
     if (step + 1 < nsteps) fetch(step + 1);
@@ -419,11 +432,11 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
       const v4s_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) v4s_t*)(vl + 16 * VRS * 16 + nt * 32));
       const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo4), h2 = __builtin_bit_cast(u32x2_t, hi4);
-      return as_bf16x8(u32x4_t{l2.x, l2.y, h2.x, h2.y});
+      return u32x4_t{l2.x, l2.y, h2.x, h2.y};
     };
     __builtin_amdgcn_s_setprio(0);
     // softmax: exponent arguments s * c - m (the causal mask only on steps
-    // that reach past some row's position), lazy reference point, P split
+    // that reach past some row's position), lazy reference point
     const bool diag = step * kStep + kStep - 1 > wmin;
     float x[2][8];
 #pragma unroll
@@ -463,25 +476,27 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
         m_run[h] = m_new;
       }
     }
-    bf16x8_t phi[2], plo[2];
+    float pw[2][8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float pw[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pw[i] = __builtin_amdgcn_exp2f(fmaf(x[h][i], c, -m_run[h]));
-      l_run[h] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
-      split_weights(pw, phi[h], plo[h]);
+      for (int i = 0; i < 8; ++i) pw[h][i] = __builtin_amdgcn_exp2f(fmaf(x[h][i], c, -m_run[h]));
+      l_run[h] += ((pw[h][0] + pw[h][1]) + (pw[h][2] + pw[h][3])) +
+                  ((pw[h][4] + pw[h][5]) + (pw[h][6] + pw[h][7]));
     }
-    // O += P V, V's operand of each output tile read just before its four MFMAs
+    // O += P V: fp16 weights (in [0, 256]: 11 significant bits) times the
+    // scaled fp16 V, float32 accumulation; V's operand of each output tile
+    // read just before its MFMAs
+    f16x8_t ph[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ph[h] = weights_f16(pw[h]);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int nt = 0; nt < DV; ++nt) {
-      const bf16x8_t b = vop(nt);
+      const f16x8_t b = as_f16x8(vop(nt));
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        acc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[h], b, acc[h][nt], 0, 0, 0);
-        acc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[h], b, acc[h][nt], 0, 0, 0);
-      }
+      for (int h = 0; h < 2; ++h)
+        acc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[h], b, acc[h][nt], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   }
@@ -499,8 +514,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
       const int rr = wave * 32 + h * 16 + 4 * grp + r;
       if (rr >= jn * G) continue;
       const int tk = rr / G, hd = rr - tk * G;
-      // a row that sees a key has l >= 1 (its largest weight is >= 1)
-      const float inv = base + tk >= 0 ? 1.0f / l_c : 0.f;
+      // a row that sees a key has l >= 1 (its largest weight is >= 1); the
+      // factor 2^4 undoes V's scaling
+      const float inv = base + tk >= 0 ? (1.0f / kVScale) / l_c : 0.f;
       float* dst = p.out + ((int64_t)(q0 + j0 + tk) * p.num_q_heads + (int64_t)kvh * G + hd) * D +
                    col;
       // streaming stores: the output is not read back here, and the lines

@@ -6,7 +6,9 @@ attends causally to everything before it through the block table.  Checked
 against the oracle's prefill_attention, element by element, at the full
 chunked-prefill workload too (16 sequences, 6877 query tokens: the oracle
 takes seconds).  Bar: max |gpu - oracle| <= 2e-3 (bf16 K/V/Q, float32
-accumulation), pools bit-exact.
+accumulation), pools bit-exact.  P V runs in fp16 (weights rounded to 11
+significant bits, V scaled by 2^-4): its range is checked with V scaled far
+up and far down.
 """
 
 from __future__ import annotations
@@ -146,3 +148,37 @@ def test_prefill_more_pairs_than_the_sort_takes():
                             np.ones(S, np.int64), 8, 8, 64, 16, rng=rng)
     dev, out = _run(wl)
     _check(wl, dev, out)
+
+
+def _scale_v(wl, f):
+    """The workload with every written V row multiplied by f (rounded to
+    bf16): same keys, queries and placement."""
+    w2 = copy.copy(wl)
+
+    def scaled(ops):
+        out = []
+        for kind, x in ops:
+            if kind == "write":
+                v = (O.to_f64(x.v, wl.dtype) * f).astype(np.float32)
+                x = W.Write(x.table, x.seq_ids, x.positions, x.k, W.f32_to_bf16_bits(v))
+            out.append((kind, x))
+        return out
+
+    w2.setup, w2.step = scaled(wl.setup), scaled(wl.step)
+    w2.name = f"{wl.name} V x {f:g}"
+    return w2
+
+
+@pytest.mark.parametrize("f", [3e4, 1e-3])
+def test_prefill_value_range(f):
+    """P V runs on the fp16 matrix cores with V scaled by 2^-4: values far
+    beyond fp16's 65504 (here up to ~1.5e5) and values mostly below 2^-10
+    (fp16 subnormals after scaling) keep the decode's bar relative to the
+    size of V: max |gpu - oracle| <= 2e-3 * f."""
+    wl = _scale_v(_custom(np.random.default_rng(11), [300, 17], [200, 64], 32, 8, 128, 16), f)
+    dev, out = _run(wl)
+    kp, vp, ref, _ = run_oracle(wl, wl.setup + wl.step)
+    assert np.isfinite(out).all()
+    err = max_abs_err(out, ref)
+    _say(f"  max_abs_err={err:.3e} (bar {TOL * f:.3e})")
+    assert err <= TOL * f
