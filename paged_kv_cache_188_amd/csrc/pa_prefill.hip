@@ -380,10 +380,19 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
     for (int nt = 0; nt < DV; ++nt) acc[h][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
 
+  // this thread's LDS slots for its K and V chunks (the same every step)
+  int kslot[CH], vslot[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = u + 128 * i;
+    kslot[i] = th * HALF + c;
+    vslot[i] = 2 * HALF + (th * 16 + c / GR) * VRS + c % GR;
+  }
   if (nsteps > 0) fetch(0);
   for (int step = 0; step < nsteps; ++step) {
     u32x4_t* buf = smem[step & 1];
-    const int skey0 = step * kStep + th * 16;  // first key of this thread's half
+    // first key of this thread's half (the same for the whole wave)
+    const int skey0 = __builtin_amdgcn_readfirstlane(step * kStep + th * 16);
     if (skey0 + 16 > n) {  // keys past the context: V rows zeroed (wave-uniform test)
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
@@ -393,9 +402,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = u + 128 * i;
-      buf[th * HALF + c] = kreg[i];
-      buf[2 * HALF + (th * 16 + c / GR) * VRS + c % GR] = v_to_f16(vreg[i]);
+      buf[kslot[i]] = kreg[i];
+      buf[vslot[i]] = v_to_f16(vreg[i]);
     }
     lds_barrier();
     if (step + 1 < nsteps) fetch(step + 1);
