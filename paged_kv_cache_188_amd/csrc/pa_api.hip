@@ -391,6 +391,8 @@ pa_status decode_impl(float* out, const void* q, const void* k_cache, const void
       p.prefix_out = reinterpret_cast<float*>(wsb + ws.prefix_out_off);
       p.prefix_lse = reinterpret_cast<float*>(wsb + ws.prefix_lse_off);
       p.lse_out = reinterpret_cast<float*>(wsb + ws.lse_off);
+      p.group_ws = reinterpret_cast<int32_t*>(wsb + ws.group_off);
+      p.own_ws = reinterpret_cast<int32_t*>(wsb + ws.own_off);
       p.group_start = group_start;
       p.shared_len = shared_len;
       p.num_groups = num_groups;

@@ -606,6 +606,15 @@ __global__ __launch_bounds__(kDecodeWaves * kWave, 2) void decode_mfma_streamk_k
   tile_prefix<MODE>(p, s_prefix, s_aux);
   const int Hkv = p.num_kv_heads;
   const int G = p.group;
+  // the pass's per-group / per-sequence data, for the merge and combine
+  // kernels that follow (one workgroup writes it)
+  if constexpr (MODE != kPlain) {
+    if (blockIdx.x == 0) {
+      int32_t* dst = MODE == kPrefix ? p.group_ws : p.own_ws;
+      const int n = MODE == kPrefix ? 3 * S : S;
+      for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = s_aux[i];
+    }
+  }
   // sequences with nothing to attend in the pass: zeros (and a log-sum-exp
   // of -inf), spread over the workgroups; a group with no shared tokens
   // writes nothing (its members' prefix results are not used)
@@ -831,9 +840,8 @@ __global__ __launch_bounds__(256) void decode_streamk_merge_kernel(const DecodeP
   float* out = p.out;
   float* lse = MODE == kOwn ? p.lse_out : nullptr;
   if constexpr (MODE == kPrefix) {  // a group: its members' prefix results
-    const GroupInfo gi = group_info(p, seq);
-    heads = gi.count * G;
-    row0 = (int64_t)gi.first * p.num_q_heads + kvh * G;
+    heads = p.group_ws[p.num_groups + seq] * G;
+    row0 = (int64_t)p.group_ws[seq] * p.num_q_heads + kvh * G;
     member_rows = p.num_q_heads;
     out = p.prefix_out;
     lse = p.prefix_lse;
@@ -887,21 +895,8 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_shared_combine_kernel(const DecodeParams p) {
   constexpr int C = D / 4;
   const int seq = blockIdx.x;
-  // the group holding seq: the last g with group_start[g] <= seq (bounded
-  // search; groups are consecutive ranges of sequences)
-  int lo = 0, hi = p.num_groups - 1, g = -1;
-  while (lo <= hi) {
-    const int mid = (lo + hi) / 2;
-    if (p.group_start[mid] <= seq) {
-      g = mid;
-      lo = mid + 1;
-    } else {
-      hi = mid - 1;
-    }
-  }
-  if (g < 0) return;
-  const GroupInfo gi = group_info(p, g);
-  if (gi.count == 0 || seq < gi.first || seq >= gi.first + gi.count) return;
+  // only members of a sharing group have a prefix result (own start > 0)
+  if (p.own_ws[seq] <= 0) return;
   const int64_t r0 = (int64_t)seq * p.num_q_heads;
   for (int idx = threadIdx.x; idx < p.num_q_heads * C; idx += blockDim.x) {
     const int hd = idx / C, c = idx % C;
@@ -1312,14 +1307,17 @@ DecodeWorkspace decode_workspace_partition(int num_seqs, int num_q_heads, int he
 
 DecodeWorkspace decode_workspace_shared(int num_seqs, int num_q_heads, int head_dim) {
   // stream-K partials with 16 heads per slot (the prefix pass's widest
-  // segments; the own-token pass reuses them), then the prefix results and
-  // the log2-sum-exp of both passes
+  // segments; the own-token pass reuses them), then the prefix results, the
+  // log2-sum-exp of both passes, and the passes' per-group and per-sequence
+  // data for the kernels after them
   DecodeWorkspace w = decode_workspace_streamk(num_seqs, 16, head_dim);
   const size_t rows = (size_t)num_seqs * num_q_heads;
   w.prefix_out_off = w.total;
   w.prefix_lse_off = w.prefix_out_off + align256(rows * head_dim * sizeof(float));
   w.lse_off = w.prefix_lse_off + align256(rows * sizeof(float));
-  w.total = w.lse_off + align256(rows * sizeof(float));
+  w.group_off = w.lse_off + align256(rows * sizeof(float));
+  w.own_off = w.group_off + align256((size_t)3 * kSharedMaxGroups * sizeof(int32_t));
+  w.total = w.own_off + align256((size_t)num_seqs * sizeof(int32_t));
   return w;
 }
 

@@ -87,6 +87,10 @@ struct DecodeParams {
   float* prefix_out;           // [S][Hq][D]: each member's attention over its group's prefix
   float* prefix_lse;           // [S][Hq]: its log2-sum-exp
   float* lse_out;              // [S][Hq]: log2-sum-exp of the own-token pass's `out`
+  int32_t* group_ws;           // written by the prefix pass: [3][num_groups] each group's
+                               // first member, members read together, shared tokens used
+  int32_t* own_ws;             // written by the own-token pass: [S] each sequence's first
+                               // own position (0: not in a sharing group)
 };
 
 // Stream-K decomposition limits.
@@ -116,7 +120,8 @@ hipError_t launch_prefill(const DecodeParams& p, const int32_t* query_start, int
 
 // Workspace offsets (bytes); shared by the size query and the launch.
 struct DecodeWorkspace {
-  size_t m_off, l_off, acc_off, handoff_off, prefix_out_off, prefix_lse_off, lse_off, total;
+  size_t m_off, l_off, acc_off, handoff_off, prefix_out_off, prefix_lse_off, lse_off, group_off,
+      own_off, total;
 };
 DecodeWorkspace decode_workspace_partition(int num_seqs, int num_q_heads, int head_dim,
                                            int max_partitions);
