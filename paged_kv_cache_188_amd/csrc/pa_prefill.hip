@@ -62,11 +62,12 @@
 // Occupancy: K operands are read from LDS one 32-dim slice at a time and V
 // operands one output tile at a time, right before their MFMAs, which keeps
 // the kernel at 168 registers: three workgroups per CU (three waves per
-// SIMD) instead of two; the waves raise their priority while they issue
-// matrix-core work (s_setprio), so a SIMD's matrix core is fed first.
-// (Measured: 417 -> 397 us with three workgroups per CU, -> 388 us with the
-// priority; interleaving one row half's P V with the other half's softmax
-// inside a wave, or one barrier per two steps, gained nothing.)
+// SIMD) instead of two.  (Measured: 417 -> 397 us with three workgroups per
+// CU; with two and no spills the fp16 kernel runs 10 % slower.  Raising a
+// wave's priority while it issues matrix-core work helped when P V ran on
+// the hi + lo pair, 397 -> 388 us, and costs ~1 % since the vector ALU is
+// the larger share; interleaving one row half's P V with the other half's
+// softmax inside a wave, or one barrier per two steps, gained nothing.)
 // Scheduling: the work of a (sequence, query tile) pair is its number of key
 // steps, known only from device data.  Each workgroup first ranks all pairs
 // by decreasing work (a bucketed counting sort in LDS, the same in every
@@ -416,7 +417,6 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int h = 0; h < 2; ++h) sc[kh][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    __builtin_amdgcn_s_setprio(1);  // matrix-core phase: issue ahead of the vector work
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       bf16x8_t a[2];
@@ -442,7 +442,6 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
       const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo4), h2 = __builtin_bit_cast(u32x2_t, hi4);
       return u32x4_t{l2.x, l2.y, h2.x, h2.y};
     };
-    __builtin_amdgcn_s_setprio(0);
     // softmax: exponent arguments s * c - m (the causal mask only on steps
     // that reach past some row's position), lazy reference point
     const bool diag = step * kStep + kStep - 1 > wmin;
@@ -498,7 +497,6 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
     f16x8_t ph[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) ph[h] = weights_f16(pw[h]);
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int nt = 0; nt < DV; ++nt) {
       const f16x8_t b = as_f16x8(vop(nt));
@@ -506,7 +504,6 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
       for (int h = 0; h < 2; ++h)
         acc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[h], b, acc[h][nt], 0, 0, 0);
     }
-    __builtin_amdgcn_s_setprio(0);
   }
 
   // normalise and store: acc[h][nt][r] is row wave*32 + 16h + 4*grp + r,
