@@ -147,6 +147,12 @@ __device__ __forceinline__ u32x4_t v_to_f16(u32x4_t v) {
 // half's first position and phys its physical block.  Every address is
 // inside the pools; V rows past the context are zeroed when stored to LDS
 // (not here: a select on the loaded value would wait for the load).
+// The loads go through buffer descriptors of the (block, KV head) chunk,
+// built in scalar registers: the lane supplies only its fixed 32-bit offset
+// and the half's position in the block is a scalar offset, so a step's
+// addresses cost no vector instructions.
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, no format conversion
+
 template <int D, int BS>
 __device__ __forceinline__ void load_step(const uint16_t* kpool, const uint16_t* vpool, int phys,
                                           int hkv, int kvh, int key0,
@@ -155,12 +161,17 @@ __device__ __forceinline__ void load_step(const uint16_t* kpool, const uint16_t*
                                           u32x4_t (&kreg)[D / 64], u32x4_t (&vreg)[D / 64]) {
   const int o = key0 % BS;
   const int64_t cb = ((int64_t)phys * hkv + kvh) * ((int64_t)BS * D);
-  const char* kb = reinterpret_cast<const char*>(kpool + cb + o * 8);
-  const char* vb = reinterpret_cast<const char*>(vpool + cb + (int64_t)o * D);
+  constexpr int kChunkBytes = BS * D * 2;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kpool + cb), 0, kChunkBytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vpool + cb), 0, kChunkBytes, kBufferWord3);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
-    kreg[i] = *reinterpret_cast<const u32x4_t*>(kb + (size_t)koff[i]);
-    vreg[i] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)voff[i]);
+    kreg[i] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)koff[i], o * 16, 0));
+    vreg[i] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, (int)voff[i], o * D * 2, 0));
   }
 }
 
@@ -485,18 +496,23 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
     }
     float pw[2][8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pw[h][i] = __builtin_amdgcn_exp2f(fmaf(x[h][i], c, -m_run[h]));
-      l_run[h] += ((pw[h][0] + pw[h][1]) + (pw[h][2] + pw[h][3])) +
-                  ((pw[h][4] + pw[h][5]) + (pw[h][6] + pw[h][7]));
-    }
     // O += P V: fp16 weights (in [0, 256]: 11 significant bits) times the
     // scaled fp16 V, float32 accumulation; V's operand of each output tile
-    // read just before its MFMAs
+    // read just before its MFMAs.  The running sums add the same rounded
+    // weights, two per dot-product instruction, in float32.
     f16x8_t ph[2];
+    const f16x2_t ones = f16x2_t{(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) ph[h] = weights_f16(pw[h]);
+    for (int h = 0; h < 2; ++h) {
+      ph[h] = weights_f16(pw[h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        l_run[h] = __builtin_amdgcn_fdot2(f16x2_t{ph[h][2 * i], ph[h][2 * i + 1]}, ones, l_run[h],
+                                          false);
+    }
 #pragma unroll
     for (int nt = 0; nt < DV; ++nt) {
       const f16x8_t b = as_f16x8(vop(nt));
