@@ -71,12 +71,14 @@
 // Scheduling: the work of a (sequence, query tile) pair is its number of key
 // steps, known only from device data.  Each workgroup first ranks all pairs
 // by decreasing work (a bucketed counting sort in LDS, the same in every
-// workgroup) and takes the pair at its own id's rank: workgroups start in id
-// order, so the longest items start first and the short ones fill the end.
-// (Measured: the share of workgroup slots in use over the kernel's life was
-// 0.52 with pairs in sequence order, the long items of late sequences forming
-// the tail, and 0.89 longest first.)  The KV heads of a pair take
-// consecutive ids.
+// workgroup, its counts combined with block-wide prefix sums) and takes the
+// pair at its own id's rank: workgroups start in id order, so the longest
+// items start first and the short ones fill the end.  (Measured: the share
+// of workgroup slots in use over the kernel's life was 0.52 with pairs in
+// sequence order, the long items of late sequences forming the tail, and
+// 0.89 longest first; the ranking itself costs the call ~3 us, against ~31
+// us when one thread walked the bucket and per-thread counts.)  The KV heads
+// of a pair take consecutive ids.
 
 #include "pa_internal.h"
 
@@ -210,69 +212,100 @@ __device__ __forceinline__ int pair_work(const DecodeParams& p, const int32_t* q
   return last < 0 ? 1 : last / kStep + 2;
 }
 
+// Inclusive prefix sum of v over the workgroup's threads in thread order
+// (each wave scans with shuffles; the four wave totals go through `tmp`, 4
+// ints of LDS).  Every thread of the workgroup takes part.
+__device__ __forceinline__ int block_scan(int v, int* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) tmp[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) v += tmp[w];
+  __syncthreads();  // `tmp` may be reused
+  return v;
+}
+
 // The pair at position `rank` when the pairs are ordered by decreasing work
 // (bucketed into kBuckets levels, ties in index order): workgroups are
 // dispatched in id order, so the longest work starts first and the short
 // items fill in at the end (longest-processing-time-first).  Every thread of
 // the workgroup takes part and gets the answer; `sm` is kBuckets + kThreads
-// + 4 ints of LDS.
+// + 8 ints of LDS.  The counts are combined with block-wide prefix sums, so
+// no thread walks the buckets or the other threads' counts one by one.
 __device__ int longest_first_pair(const DecodeParams& p, const int32_t* query_start,
                                   int64_t total_q, int tq, int qtiles, int P, int rank, int* sm) {
-  const int tid = threadIdx.x;
+  static_assert(kBuckets == kThreads, "one bucket per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int* hist = sm;                   // [kBuckets]
-  int* part = sm + kBuckets;        // [kThreads]
-  int* res = part + kThreads;       // [4]
+  int* res = sm + kBuckets;         // [4]
+  int* tmp = res + 4;               // [4]
+  // Each thread takes a contiguous slice of the pairs (so index order is kept)
+  // and computes the works of its first kCached pairs once.
+  constexpr int kCached = 8;
+  const int chunk = (P + kThreads - 1) / kThreads;
+  const int lo = min(P, tid * chunk), hi = min(P, lo + chunk);
+  int wk[kCached];
   int wmax = 0;
-  for (int i = tid; i < P; i += kThreads)
-    wmax = max(wmax, pair_work(p, query_start, total_q, tq, qtiles, i));
-  part[tid] = wmax;
-  for (int b = tid; b < kBuckets; b += kThreads) hist[b] = 0;
-  __syncthreads();
-  if (tid == 0) {
-    int m = 0;
-    for (int t = 0; t < kThreads; ++t) m = max(m, part[t]);
-    res[0] = m;
+#pragma unroll
+  for (int k = 0; k < kCached; ++k) {
+    wk[k] = lo + k < hi ? pair_work(p, query_start, total_q, tq, qtiles, lo + k) : 0;
+    wmax = max(wmax, wk[k]);
   }
+  for (int i = lo + kCached; i < hi; ++i)
+    wmax = max(wmax, pair_work(p, query_start, total_q, tq, qtiles, i));
+  // the largest work of any pair
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wmax = max(wmax, __shfl_xor(wmax, o));
+  hist[tid] = 0;
+  if (lane == 0) tmp[wave] = wmax;
   __syncthreads();
-  wmax = res[0];
+  wmax = max(max(tmp[0], tmp[1]), max(tmp[2], tmp[3]));
   auto bucket = [&](int w) {
     return w == 0 ? 0 : 1 + (int)((int64_t)(w - 1) * (kBuckets - 2) / max(wmax - 1, 1));
   };
-  for (int i = tid; i < P; i += kThreads)
+  auto work_at = [&](int k) {  // work of pair lo + k
+    return k < kCached ? wk[k] : pair_work(p, query_start, total_q, tq, qtiles, lo + k);
+  };
+#pragma unroll
+  for (int k = 0; k < kCached; ++k)
+    if (lo + k < hi) atomicAdd(&hist[bucket(wk[k])], 1);
+  for (int i = lo + kCached; i < hi; ++i)
     atomicAdd(&hist[bucket(pair_work(p, query_start, total_q, tq, qtiles, i))], 1);
   __syncthreads();
-  if (tid == 0) {  // the bucket holding `rank`, buckets taken from the top
-    int start = 0, b = kBuckets - 1;
-    for (; b > 0 && start + hist[b] <= rank; --b) start += hist[b];
-    res[1] = b;
-    res[2] = rank - start;  // position inside the bucket
+  // the bucket holding `rank`, buckets taken from the top: thread t holds
+  // bucket kBuckets-1-t, and the one whose running count first passes
+  // `rank` has it
+  {
+    const int h = hist[kBuckets - 1 - tid];
+    const int cum = block_scan(h, tmp);
+    if (cum > rank && cum - h <= rank) {
+      res[0] = kBuckets - 1 - tid;
+      res[1] = rank - (cum - h);  // position inside the bucket
+    }
   }
   __syncthreads();
-  const int tb = res[1], want = res[2];
-  const int chunk = (P + kThreads - 1) / kThreads;  // contiguous slices keep index order
-  const int lo = min(P, tid * chunk), hi = min(P, lo + chunk);
+  const int tb = res[0], want = res[1];
+  // the thread whose slice holds that position, then its element
   int cnt = 0;
-  for (int i = lo; i < hi; ++i)
+#pragma unroll
+  for (int k = 0; k < kCached; ++k) cnt += lo + k < hi && bucket(wk[k]) == tb;
+  for (int i = lo + kCached; i < hi; ++i)
     cnt += bucket(pair_work(p, query_start, total_q, tq, qtiles, i)) == tb;
-  part[tid] = cnt;
-  __syncthreads();
-  if (tid == 0) {
-    int before = 0, t = 0;
-    for (; t < kThreads - 1 && before + part[t] <= want; ++t) before += part[t];
-    res[1] = t;
-    res[2] = want - before;
-  }
-  __syncthreads();
-  if (tid == res[1]) {
-    int k = res[2];
+  const int cum = block_scan(cnt, tmp);
+  if (cum > want && cum - cnt <= want) {
+    int k = want - (cum - cnt);
     for (int i = lo; i < hi; ++i)
-      if (bucket(pair_work(p, query_start, total_q, tq, qtiles, i)) == tb && k-- == 0) {
-        res[3] = i;
+      if (bucket(work_at(i - lo)) == tb && k-- == 0) {
+        res[2] = i;
         break;
       }
   }
   __syncthreads();
-  const int pair = res[3];
+  const int pair = res[2];
   __syncthreads();  // `sm` is reused by the caller
   return pair;
 }
