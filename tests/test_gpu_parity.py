@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import climbing_cases as C
 import workloads as W
 from plan_oracle import max_abs_err, run_oracle
 
@@ -205,6 +206,25 @@ def test_streamk_splits(case):
     assert err <= TOL["bf16"]
     assert np.all(out[ctx == 0] == 0.0)
     assert np.isfinite(out).all()
+
+
+# Scores that climb along the context, and spiked keys (tests/climbing_cases):
+# the kernels' softmax reference point moves many times inside a wave's run of
+# tiles, partials of one split context carry reference points hundreds of
+# log2 units apart, and a spike's weight drowns every other key's.
+@pytest.mark.parametrize("case", C.DECODE, ids=lambda c: c[0])
+def test_climbing_scores(case):
+    wl = C.decode_case(case)
+    forms = ((None, False, False), (16, False, False), (64, False, False), (None, True, False),
+             (None, False, True))
+    for part, append, vector_only in forms:
+        out, ref = run_both(wl, partition=part, check_pools=(part is None and not vector_only),
+                            append=append, vector_only=vector_only)
+        err = max_abs_err(out, ref)
+        _say(f"  partition={part} append={append} vector_only={vector_only} "
+             f"max_abs_err={err:.3e}")
+        assert err <= TOL["bf16"]
+        assert np.isfinite(out).all() and np.all(out[wl.context_lens == 0] == 0.0)
 
 
 @pytest.mark.parametrize("num_seqs", [8192, 8193], ids=["streamk-max-batch", "partition-batch"])

@@ -20,6 +20,7 @@ import numpy as np
 import pytest
 import torch
 
+import climbing_cases as C
 import paged_kv_cache_188_amd as pa
 import workloads as W
 from oracle import paged_attention as O
@@ -88,6 +89,17 @@ def test_prefill_shapes(case):
     wl = _custom(np.random.default_rng(sum(pre) + hq), pre, chunk, hq, hkv, d, bs)
     dev, out = _run(wl)
     _check(wl, dev, out)
+
+
+@pytest.mark.parametrize("case", C.PREFILL, ids=lambda c: c[0])
+def test_prefill_climbing_scores(case):
+    """Scores that climb along the context, and spiked keys
+    (tests/climbing_cases): each query row's reference point moves many
+    times over its causal window and spikes drown the other keys' weights."""
+    wl = C.prefill_case(case)
+    dev, out = _run(wl)
+    _check(wl, dev, out)
+    assert np.isfinite(out).all()
 
 
 def test_chunk_longer_than_context_gives_zeros():

@@ -87,6 +87,16 @@ def test_shared_parity_shapes(shape):
     _check(_shared_wl(**shape), append=True)
 
 
+@pytest.mark.parametrize("append", [False, True])
+def test_shared_climbing_scores(append):
+    """Scores that climb along the context with one spiked key in the shared
+    prefix and one in the own tokens: the prefix pass and the own-token pass
+    end on reference points far apart, which the combine must reconcile."""
+    wl = W.climbing_scores(_shared_wl(prefix=160, tail=(20, 90), seed=23), slope=0.33,
+                           spike_at=(70, 200), name="shared-prefix climbing scores")
+    _check(wl, append)
+
+
 def test_shared_full_size_sampled():
     """The full shared-prefix workload (32 prompts x 8 samples, prefix 2048)
     in the benchmark's launch configuration; sampled outputs."""

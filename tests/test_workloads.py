@@ -99,3 +99,35 @@ def test_shared_prefix_accounting():
         assert len({int(pre[r, npb - 1]) for r in rows}) == 1
     # unique KV is well below the logical KV: the prefix is stored once per group
     assert w.unique_kv_bytes() < w.kv_bytes_read()
+
+
+def test_climbing_inputs_move_the_reference_point():
+    """The climbing-score workloads the GPU parity tests run do what they are
+    for: along the longest context the reference point of a lazy softmax
+    (slack 8 in log2, 16-key tiles) moves many times -- about once per 8
+    log2 of rise where only the ramp lifts the scores, at least 4 times where
+    spikes lift the reference point above the ramp for a while -- and every
+    spiked key outweighs every key that is not spiked by >= 2^30."""
+    import climbing_cases as C
+    for case in C.DECODE:
+        wl = C.decode_case(case)
+        slope, spikes = case[6], case[7]
+        s = int(np.argmax(wl.context_lens))
+        n = int(wl.context_lens[s])
+        for h in (0, wl.num_q_heads - 1):
+            sc = C.log2_scores(wl, wl.q[s], s, h)
+            if slope:
+                # the expected rise over the context, in steps of the slack
+                want = 0.5 * slope * n / C.LAZY_SLACK if not spikes else 4
+                assert C.reference_moves(sc) >= want, (case[0], h)
+            plain = np.delete(sc, [p for p in spikes if p < n])
+            for p in spikes:
+                if p < n and not slope:
+                    assert sc[p] - plain.max() >= 30, (case[0], p)
+    for case in C.PREFILL:
+        wl = C.prefill_case(case)
+        s = int(np.argmax(wl.context_lens))
+        last = int(wl.query_start[s + 1]) - 1
+        sc = C.log2_scores(wl, wl.q[last], s, 0)
+        want = 0.5 * case[7] * sc.size / C.LAZY_SLACK if not case[8] else 4
+        assert C.reference_moves(sc) >= want, case[0]

@@ -523,3 +523,55 @@ def make_cow_observable(small: bool = True) -> Workload:
                                       tail_lo=3, tail_hi=40, cow_in_step=False)
     return shared_prefix_workload("shared-prefix CoW-observable prefix=2040", rng=rng,
                                   seed=seed, prefix=2040, cow_in_step=False)
+
+
+# ---------------------------------------------------------------------------
+# inputs whose attention scores climb along the context
+# ---------------------------------------------------------------------------
+
+def _bits_to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == BF16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return x.astype(np.float32)
+
+
+def _f32_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == BF16 else x.astype(np.float32)
+
+
+def climbing_scores(wl: Workload, *, slope: float = 0.0, spike_at=(), spike_gain: float = 8.0,
+                    name: str = None) -> Workload:
+    """A copy of ``wl`` whose scores rise with the key position.
+
+    Every query element is made non-negative (|q|) and the key row stored at
+    logical position p becomes ``|k| * g + c * p`` (rounded once to the
+    element type), with g = ``spike_gain`` at the positions in ``spike_at``
+    and 1 elsewhere.  c is chosen so that the expected score, in log2 units
+    (score * scale / ln 2), grows by ``slope`` per position: with
+    E|q_d| = sqrt(2/pi), c = slope / (scale * log2(e) * sqrt(2/pi) * D).
+    Such inputs move any softmax reference point again and again along the
+    context, and a spiked key outweighs every other by many powers of two.
+    Placement, V rows, tables and lengths are unchanged."""
+    import copy
+    w2 = copy.copy(wl)
+    w2.q = _f32_to_bits(np.abs(_bits_to_f32(wl.q, wl.dtype)), wl.dtype)
+    c = slope / (wl.scale * math.log2(math.e) * math.sqrt(2.0 / math.pi) * wl.head_dim)
+    spikes = np.asarray(sorted(spike_at), dtype=np.int64)
+
+    def steer(ops):
+        out = []
+        for kind, x in ops:
+            if kind == "write":
+                p = x.positions.astype(np.float32)[:, None, None]
+                g = np.where(np.isin(x.positions, spikes), np.float32(spike_gain),
+                             np.float32(1.0))[:, None, None]
+                k = np.abs(_bits_to_f32(x.k, wl.dtype)) * g + np.float32(c) * p
+                x = Write(x.table, x.seq_ids, x.positions, _f32_to_bits(k, wl.dtype), x.v)
+            out.append((kind, x))
+        return out
+
+    w2.setup, w2.step = steer(wl.setup), steer(wl.step)
+    w2.tables = dict(wl.tables)
+    w2.notes = dict(wl.notes)
+    w2.name = name or f"{wl.name} climbing scores slope={slope:g} spikes={len(spikes)}"
+    return w2
