@@ -517,6 +517,36 @@ def history_write_timing(torch, dev, wl, stream, reps=5):
     return out
 
 
+def block_copy_reference(torch, pa, stream, reps=10):
+    """What a read + write stream reaches on this machine through libpa's own
+    block copy: 8192 blocks of 64 KiB (K and V, 32 KiB each) copied from one
+    half of a pool pair into the other, 512 MiB read and 512 MiB written per
+    call, once with the blocks in order and once with source and destination
+    blocks in two seeded random orders (the scattered placement a history
+    write stores into).  One event pair around reps back-to-back calls each."""
+    nb, hkv, bs, d = 16384, 8, 16, 128
+    k = torch.zeros((nb, hkv, d // 8, bs, 8), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((nb, hkv, bs, d), dtype=torch.bfloat16, device="cuda")
+    half = nb // 2
+    g = torch.Generator().manual_seed(188)
+    orders = {"sequential": (torch.arange(half), torch.arange(half) + half),
+              "shuffled": (torch.randperm(half, generator=g),
+                           torch.randperm(half, generator=g) + half)}
+    nbytes = 2 * 2 * half * hkv * bs * d * 2  # K and V, read and written
+    out = {"blocks": half, "block_bytes": 2 * hkv * bs * d * 2,
+           "bytes_read_plus_written": nbytes}
+    for name, (src, dst) in orders.items():
+        pairs = torch.stack([src, dst], 1).to(torch.int32).cuda()
+        pa.copy_blocks(k, v, pairs, stream=stream)
+        ms = _span_ms(torch, stream, lambda r: pa.copy_blocks(k, v, pairs, stream=stream), reps)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 1), "gbps": round(gbps, 1),
+                     "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    del k, v
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_result(cid, args, cpu_seconds, separate=False, shared=False):
     """One decode workload: the step timed over rotated pool copies, the
     decode call's roofline, single-call distribution, probes, the step's
@@ -884,6 +914,8 @@ def main():
           flush=True)
     out = _driver_keys(head, args)
     out["sub_results"] = subs
+    import paged_kv_cache_188_amd as pa
+    out["read_write_reference"] = block_copy_reference(torch, pa, torch.cuda.current_stream())
     print(json.dumps(out), flush=True)
 
 

@@ -29,6 +29,15 @@ __device__ __forceinline__ void store_stream(uint8_t* p, uint4 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(p));
 }
 
+// Streaming (non-temporal) 16-byte load, for rows read exactly once.
+// Measured on MI355X (history writes of 131k / 338k / 524k tokens by the
+// run kernel below): 1-3 % faster than ordinary loads, which leave the
+// source rows in L2 and the Infinity Cache in place of lines still useful.
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+  return __builtin_bit_cast(uint4,
+                            __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
 // Slot of token j (-1: padding, or an index outside its table or the pool).
 __device__ __forceinline__ int64_t token_slot(const int32_t* __restrict__ block_tables,
                                               int num_seqs, int max_blocks_per_seq,
@@ -268,8 +277,8 @@ __global__ __launch_bounds__(kRunThreads) void write_kv_runs_kernel(
         kx[u] = vx[u] = make_uint4(0u, 0u, 0u, 0u);
         if (e < total) {
           const int64_t src = (int64_t)(j0 + s_tok[i]) * token_stride_bytes + (int64_t)c * 16;
-          kx[u] = *reinterpret_cast<const uint4*>(k_new + src);
-          vx[u] = *reinterpret_cast<const uint4*>(v_new + src);
+          kx[u] = load_stream(k_new + src);
+          vx[u] = load_stream(v_new + src);
         }
       }
 #pragma unroll
@@ -308,8 +317,8 @@ __global__ __launch_bounds__(kRunThreads) void write_kv_runs_kernel(
       a[t] = b[t] = make_uint4(0u, 0u, 0u, 0u);
       if (s_slot[1 + t0 + t] < 0) continue;
       const int64_t src = (int64_t)(j0 + t0 + t) * token_stride_bytes + (int64_t)c * 16;
-      a[t] = *reinterpret_cast<const uint4*>(k_new + src);
-      b[t] = *reinterpret_cast<const uint4*>(v_new + src);
+      a[t] = load_stream(k_new + src);
+      b[t] = load_stream(v_new + src);
     }
 #pragma unroll
     for (int t = 0; t < kRunWaveTokens; ++t) {
