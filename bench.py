@@ -521,9 +521,11 @@ def block_copy_reference(torch, pa, stream, reps=10):
     """What a read + write stream reaches on this machine through libpa's own
     block copy: 8192 blocks of 64 KiB (K and V, 32 KiB each) copied from one
     half of a pool pair into the other, 512 MiB read and 512 MiB written per
-    call, once with the blocks in order and once with source and destination
-    blocks in two seeded random orders (the scattered placement a history
-    write stores into).  One event pair around reps back-to-back calls each."""
+    call: with the blocks in order; with source and destination blocks in
+    two seeded random orders; and with the sources in order and the
+    destinations in a random order, the pattern of a history write (rows
+    read in order, stored into scattered blocks).  One event pair around reps
+    back-to-back calls each."""
     nb, hkv, bs, d = 16384, 8, 16, 128
     k = torch.zeros((nb, hkv, d // 8, bs, 8), dtype=torch.bfloat16, device="cuda")
     v = torch.zeros((nb, hkv, bs, d), dtype=torch.bfloat16, device="cuda")
@@ -531,7 +533,9 @@ def block_copy_reference(torch, pa, stream, reps=10):
     g = torch.Generator().manual_seed(188)
     orders = {"sequential": (torch.arange(half), torch.arange(half) + half),
               "shuffled": (torch.randperm(half, generator=g),
-                           torch.randperm(half, generator=g) + half)}
+                           torch.randperm(half, generator=g) + half),
+              "sequential_to_shuffled": (torch.arange(half),
+                                         torch.randperm(half, generator=g) + half)}
     nbytes = 2 * 2 * half * hkv * bs * d * 2  # K and V, read and written
     out = {"blocks": half, "block_bytes": 2 * hkv * bs * d * 2,
            "bytes_read_plus_written": nbytes}
