@@ -20,7 +20,8 @@
 // head r % G), 32 per wave.  The workgroup walks the keys from position 0 in
 // steps of 32 (two 16-key halves): the 256 threads copy the step's K and V
 // rows from the paged pools into LDS (double-buffered: the next step's loads
-// are in flight while the current one is used), then every wave
+// are in flight while the current one is used; K goes straight from the pool
+// into LDS, V through registers, where it is converted), then every wave
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (LDS),
 //                 B = 32 dims x 16 rows (registers, loaded once);
 //                 lane (grp = lane/16, col = lane%16) gets the scores of
@@ -53,7 +54,11 @@
 // block base plus a per-lane 32-bit offset fixed for the whole walk; V rows
 // past the context are zeroed only on the step that reaches past it, when
 // they are stored to LDS; the barrier orders LDS only, so the next step's
-// global loads stay in flight across it.  (Measured on MI355X, the
+// global loads stay in flight across it.  K rows are loaded straight into
+// LDS (buffer loads with an LDS destination), so they hold no registers
+// while in flight and need no LDS store instructions; the registers this
+// frees keep more K operand reads in flight in the score phase (measured:
+// 326-334 -> 293-303 us per call).  (Measured on MI355X, the
 // chunked-prefill workload of 16 sequences x 512-token chunks: 783 us per
 // call with one wave per 16 query rows and no K/V sharing, 605 us with this
 // layout; the vector-ALU trims -- uniform base addresses, three-way max, V
@@ -141,8 +146,9 @@ __device__ __forceinline__ u32x4_t v_to_f16(u32x4_t v) {
   return r;
 }
 
-// Global -> register loads of one 16-key half for thread u (0..127) of the
-// half: K chunk c = u + 128 i is granule c / 16 of key c % 16, V chunk c is
+// Loads of one 16-key half for thread u (0..127) of the half, K straight
+// into LDS and V into registers: K chunk c = u + 128 i is granule c / 16 of
+// key c % 16, V chunk c is
 // granule c % (D/8) of key c / (D/8); koff / voff hold the chunks' byte
 // offsets inside a block's 16 keys, so an address is the (wave-uniform)
 // base of (phys, kvh, key0 % BS) plus a 32-bit lane offset.  key0 is the
@@ -152,7 +158,10 @@ __device__ __forceinline__ u32x4_t v_to_f16(u32x4_t v) {
 // The loads go through buffer descriptors of the (block, KV head) chunk,
 // built in scalar registers: the lane supplies only its fixed 32-bit offset
 // and the half's position in the block is a scalar offset, so a step's
-// addresses cost no vector instructions.
+// addresses cost no vector instructions.  A K load with an LDS destination
+// writes lane L's 16 bytes at the (wave-uniform) LDS address + 16 L, so
+// chunk i of the wave lands at kdst + 128 i (in 16-byte units), the slots
+// the score phase reads.
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, no format conversion
 
 template <int D, int BS>
@@ -160,18 +169,19 @@ __device__ __forceinline__ void load_step(const uint16_t* kpool, const uint16_t*
                                           int hkv, int kvh, int key0,
                                           const uint32_t (&koff)[D / 64],
                                           const uint32_t (&voff)[D / 64],
-                                          u32x4_t (&kreg)[D / 64], u32x4_t (&vreg)[D / 64]) {
+                                          u32x4_t* kdst, u32x4_t (&vreg)[D / 64]) {
   const int o = key0 % BS;
   const int64_t cb = ((int64_t)phys * hkv + kvh) * ((int64_t)BS * D);
   constexpr int kChunkBytes = BS * D * 2;
-  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+  const auto kr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(kpool + cb), 0, kChunkBytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(vpool + cb), 0, kChunkBytes, kBufferWord3);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
-    kreg[i] = __builtin_bit_cast(
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)koff[i], o * 16, 0));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        kr, (__attribute__((address_space(3))) void*)(kdst + 128 * i), 16, (int)koff[i], o * 16, 0,
+        0);
     vreg[i] = __builtin_bit_cast(
         u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, (int)voff[i], o * D * 2, 0));
   }
@@ -389,12 +399,12 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
   const int last = base + jn - 1;  // the workgroup's last position (<= n - 1)
   const int nsteps = last < 0 ? 0 : last / kStep + 1;
 
-  // global -> register loads of one step: thread (half th, index u)
+  // loads of one step: thread (half th, index u)
   const int th = tid >> 7, u = tid & 127;
   const uint16_t* kpool = static_cast<const uint16_t*>(p.k_cache);
   const uint16_t* vpool = static_cast<const uint16_t*>(p.v_cache);
   const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
-  u32x4_t kreg[CH], vreg[CH];
+  u32x4_t vreg[CH];
   uint32_t koff[CH], voff[CH];  // byte offsets of this thread's chunks in a 16-key half
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -405,6 +415,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
   // block ids come 64 at a time, one per lane, and are picked with readlane:
   // the K/V loads of a step never wait for a table lookup
   int ids = 0, ids_chunk = -1;
+  // this wave's K chunks of a step land in LDS in lane order: chunk
+  // u + 128 i of its half at slot th * HALF + u + 128 i
+  const int kwave = th * HALF + 64 * ((tid >> 6) & 1);
   auto fetch = [&](int step) {
     const int key0 = __builtin_amdgcn_readfirstlane(step * kStep + th * 16);
     const int blk = key0 / BS;
@@ -413,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
       ids = load_ids<BS>(bt, ids_chunk, n, p.num_blocks, lane);
     }
     load_step<D, BS>(kpool, vpool, __builtin_amdgcn_readlane(ids, blk % 64), p.num_kv_heads, kvh,
-                     key0, koff, voff, kreg, vreg);
+                     key0, koff, voff, &smem[step & 1][kwave], vreg);
   };
   // byte offset of this lane's transposing-load source in the V tile (key
   // 4*grp + col/4, dims 4*(col%4) .. +3 of dim tile 0)
@@ -425,12 +438,11 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
     for (int nt = 0; nt < DV; ++nt) acc[h][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
 
-  // this thread's LDS slots for its K and V chunks (the same every step)
-  int kslot[CH], vslot[CH];
+  // this thread's LDS slots for its V chunks (the same every step)
+  int vslot[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = u + 128 * i;
-    kslot[i] = th * HALF + c;
     vslot[i] = 2 * HALF + (th * 16 + c / GR) * VRS + c % GR;
   }
   if (nsteps > 0) fetch(0);
@@ -446,10 +458,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_flash_kernel(
       }
     }
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      buf[kslot[i]] = kreg[i];
-      buf[vslot[i]] = v_to_f16(vreg[i]);
-    }
+    for (int i = 0; i < CH; ++i) buf[vslot[i]] = v_to_f16(vreg[i]);
+    // this wave's K chunks, loaded straight into LDS, have landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     lds_barrier();
     if (step + 1 < nsteps) fetch(step + 1);
     if (step * kStep > wmax) continue;  // nothing left for this wave's rows
