@@ -71,7 +71,8 @@ def _custom(rng, pre, chunk, hq, hkv, d, bs):
 # (prefix lengths, chunk lengths, Hq, Hkv, D, bs): every group size G = 1, 2,
 # 4, 6, 8, 16 (128 / G chunk tokens per workgroup, 128 - 128 % G rows used),
 # both head dims, every block size, empty chunks, one-token chunks, chunks
-# starting at position 0, contexts over 64 blocks, a 2048-token chunk
+# starting at position 0, contexts over 64 blocks (of 16, 32 and 64 tokens),
+# a 2048-token chunk
 EDGE = [
     ([0, 40, 3], [37, 16, 1], 8, 8, 64, 32),
     ([100, 0, 17], [64, 0, 129], 16, 8, 128, 16),
@@ -80,6 +81,10 @@ EDGE = [
     ([0, 1100], [21, 40], 16, 1, 64, 16),
     ([1500, 0], [300, 200], 32, 8, 128, 16),
     ([2000, 37], [2048, 700], 16, 2, 128, 32),   # a 2048-token chunk over a long prefix
+    # 64-token blocks past 64 blocks (4096 positions): the walk crosses a
+    # chunk of 64 table entries
+    ([4200, 3], [300, 90], 8, 8, 64, 64),
+    ([4100, 0], [64, 129], 32, 8, 128, 64),
 ]
 
 
