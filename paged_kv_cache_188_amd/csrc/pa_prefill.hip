@@ -64,15 +64,18 @@
 // layout; the vector-ALU trims -- uniform base addresses, three-way max, V
 // zeroing on one step, transposing V loads instead of byte permutes -- took
 // a further 17 %.)
-// Occupancy: K operands are read from LDS one 32-dim slice at a time and V
-// operands one output tile at a time, right before their MFMAs, which keeps
-// the kernel at 168 registers: three workgroups per CU (three waves per
-// SIMD) instead of two.  (Measured: 417 -> 397 us with three workgroups per
-// CU; with two and no spills the fp16 kernel runs 10 % slower.  Raising a
-// wave's priority while it issues matrix-core work helped when P V ran on
-// the hi + lo pair, 397 -> 388 us, and costs ~1 % since the vector ALU is
-// the larger share; interleaving one row half's P V with the other half's
-// softmax inside a wave, or one barrier per two steps, gained nothing.)
+// Occupancy: K and V operands are read from LDS shortly before their MFMAs
+// (a few slices or output tiles in flight, not the whole step), which keeps
+// the kernel within 168 registers (166 with K bypassing registers): three
+// workgroups per CU (three waves per SIMD) instead of two.  The register
+// allocation limits how many operand reads are in flight, so registers
+// freed elsewhere turn into shorter LDS waits.  (Measured: 417 -> 397 us
+// with three workgroups per CU; with two and no spills the fp16 kernel runs
+// 10 % slower.  Raising a wave's priority while it issues matrix-core work
+// helped when P V ran on the hi + lo pair, 397 -> 388 us, and costs ~1 %
+// since the vector ALU is the larger share; interleaving one row half's P V
+// with the other half's softmax inside a wave, or one barrier per two steps,
+// gained nothing.)
 // Scheduling: the work of a (sequence, query tile) pair is its number of key
 // steps, known only from device data.  Each workgroup first ranks all pairs
 // by decreasing work (a bucketed counting sort in LDS, the same in every
