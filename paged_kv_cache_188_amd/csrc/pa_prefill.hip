@@ -151,13 +151,13 @@ __device__ __forceinline__ u32x4_t v_to_f16(u32x4_t v) {
 
 // Loads of one 16-key half for thread u (0..127) of the half, K straight
 // into LDS and V into registers: K chunk c = u + 128 i is granule c / 16 of
-// key c % 16, V chunk c is
-// granule c % (D/8) of key c / (D/8); koff / voff hold the chunks' byte
-// offsets inside a block's 16 keys, so an address is the (wave-uniform)
-// base of (phys, kvh, key0 % BS) plus a 32-bit lane offset.  key0 is the
-// half's first position and phys its physical block.  Every address is
-// inside the pools; V rows past the context are zeroed when stored to LDS
-// (not here: a select on the loaded value would wait for the load).
+// key c % 16, V chunk c is granule c % (D/8) of key c / (D/8); koff / voff
+// hold the chunks' byte offsets inside a block's 16 keys, so an address is
+// the (wave-uniform) base of (phys, kvh, key0 % BS) plus a 32-bit lane
+// offset.  key0 is the half's first position and phys its physical block.
+// Every address is inside the pools; V rows past the context are zeroed
+// when stored to LDS (not here: a select on the loaded value would wait for
+// the load).
 // The loads go through buffer descriptors of the (block, KV head) chunk,
 // built in scalar registers: the lane supplies only its fixed 32-bit offset
 // and the half's position in the block is a scalar offset, so a step's
@@ -176,7 +176,7 @@ __device__ __forceinline__ void load_step(const uint16_t* kpool, const uint16_t*
   const int o = key0 % BS;
   const int64_t cb = ((int64_t)phys * hkv + kvh) * ((int64_t)BS * D);
   constexpr int kChunkBytes = BS * D * 2;
-  const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(kpool + cb), 0, kChunkBytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(vpool + cb), 0, kChunkBytes, kBufferWord3);
