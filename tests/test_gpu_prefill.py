@@ -85,6 +85,8 @@ EDGE = [
     # chunk of 64 table entries
     ([4200, 3], [300, 90], 8, 8, 64, 64),
     ([4100, 0], [64, 129], 32, 8, 128, 64),
+    # a long walk: ~2000 key steps through ~32 chunks of table entries
+    ([65000], [40], 8, 8, 128, 32),
 ]
 
 
