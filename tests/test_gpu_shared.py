@@ -82,6 +82,9 @@ def test_shared_parity_cow_observable(append):
     dict(num_q_heads=32, num_kv_heads=8, block_size=8),
     dict(num_q_heads=32, num_kv_heads=8, block_size=32),
     dict(num_q_heads=16, num_kv_heads=1, samples=3, prefix=256, tail=(1, 40)),  # G = 16: none
+    # a 20,000-token prefix: each group's prefix segment split over many
+    # waves, long merge chains in the prefix pass
+    dict(num_q_heads=32, num_kv_heads=8, samples=4, groups=2, prefix=20000, tail=(5, 300)),
 ])
 def test_shared_parity_shapes(shape):
     _check(_shared_wl(**shape), append=True)
