@@ -64,7 +64,7 @@ def key_rows(wl, seq):
         if kind != "write":
             continue
         sel = x.seq_ids == seq
-        rows[x.positions[sel]] = W._bits_to_f32(x.k[sel], wl.dtype)
+        rows[x.positions[sel]] = W.bits_to_f32(x.k[sel], wl.dtype)
     assert not np.isnan(rows).any()
     return rows
 
@@ -73,7 +73,7 @@ def log2_scores(wl, q_row, seq, head):
     """Scores of one query row of head ``head`` against every key of ``seq``,
     in log2 units (float64)."""
     k = key_rows(wl, seq)[:, head // wl.group, :]
-    q = W._bits_to_f32(q_row[head], wl.dtype).astype(np.float64)
+    q = W.bits_to_f32(q_row[head], wl.dtype).astype(np.float64)
     return (k @ q) * wl.scale / np.log(2.0)
 
 

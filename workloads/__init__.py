@@ -529,13 +529,16 @@ def make_cow_observable(small: bool = True) -> Workload:
 # inputs whose attention scores climb along the context
 # ---------------------------------------------------------------------------
 
-def _bits_to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+def bits_to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Element bits of ``dtype`` (bf16 as uint16) as float32 values (exact)."""
     if dtype == BF16:
         return (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
     return x.astype(np.float32)
 
 
-def _f32_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+def f32_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values in the element encoding of ``dtype`` (bf16: rounded to
+    nearest, ties to even)."""
     return f32_to_bf16_bits(x) if dtype == BF16 else x.astype(np.float32)
 
 
@@ -554,7 +557,7 @@ def climbing_scores(wl: Workload, *, slope: float = 0.0, spike_at=(), spike_gain
     Placement, V rows, tables and lengths are unchanged."""
     import copy
     w2 = copy.copy(wl)
-    w2.q = _f32_to_bits(np.abs(_bits_to_f32(wl.q, wl.dtype)), wl.dtype)
+    w2.q = f32_to_bits(np.abs(bits_to_f32(wl.q, wl.dtype)), wl.dtype)
     c = slope / (wl.scale * math.log2(math.e) * math.sqrt(2.0 / math.pi) * wl.head_dim)
     spikes = np.asarray(sorted(spike_at), dtype=np.int64)
 
@@ -565,8 +568,8 @@ def climbing_scores(wl: Workload, *, slope: float = 0.0, spike_at=(), spike_gain
                 p = x.positions.astype(np.float32)[:, None, None]
                 g = np.where(np.isin(x.positions, spikes), np.float32(spike_gain),
                              np.float32(1.0))[:, None, None]
-                k = np.abs(_bits_to_f32(x.k, wl.dtype)) * g + np.float32(c) * p
-                x = Write(x.table, x.seq_ids, x.positions, _f32_to_bits(k, wl.dtype), x.v)
+                k = np.abs(bits_to_f32(x.k, wl.dtype)) * g + np.float32(c) * p
+                x = Write(x.table, x.seq_ids, x.positions, f32_to_bits(k, wl.dtype), x.v)
             out.append((kind, x))
         return out
 
